@@ -1,0 +1,189 @@
+"""Centroid-scored 3D block-sparse attention for video DiTs on MI355X (gfx950).
+
+Thin binding over the C ABI of libvsa.so (include/vsa.h).  Torch provides
+device memory and the current stream; every step of the computation runs in
+the library's HIP kernels.  There is no CPU fallback: without the built
+library every call raises.
+
+    index = plan(q, k, grid=(T, H, W), block=(bt, bh, bw), density=0.2)
+    o = attn(q, k, v, index)
+
+q, k, v: contiguous CUDA tensors [B, heads, T*H*W, D], bfloat16 or float32,
+tokens in raster order (t*H + h)*W + w.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from dataclasses import dataclass
+from typing import Optional, Sequence, Tuple, Union
+
+import torch
+
+from . import _lib
+from ._lib import VsaError, VsaIndex, VsaShape, check, load
+
+__all__ = ["plan", "attn", "query", "permute", "unpermute", "centroids", "centroid_scores",
+           "Index", "VsaError", "load"]
+
+_DTYPES = {torch.bfloat16: _lib.VSA_BF16, torch.float32: _lib.VSA_F32}
+
+
+def _stream(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _shape_of(x: torch.Tensor, grid, block) -> VsaShape:
+    if x.dim() != 4:
+        raise ValueError("expected [B, heads, N, D]")
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    if not x.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not x.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    T, H, W = (int(a) for a in grid)
+    bt, bh, bw = (int(a) for a in block)
+    B, Hh, N, D = x.shape
+    if N != T * H * W:
+        raise ValueError(f"N={N} does not match grid {T}x{H}x{W}")
+    return VsaShape(B, Hh, D, T, H, W, bt, bh, bw, _DTYPES[x.dtype])
+
+
+def _densities(density, heads: int):
+    if isinstance(density, (int, float)):
+        vals = [float(density)]
+    else:
+        vals = [float(d) for d in density]
+    return (ctypes.c_float * len(vals))(*vals), len(vals)
+
+
+@dataclass
+class Index:
+    """CSR block index produced by plan(): row r = (b*heads + h)*nb + i."""
+    shape: VsaShape
+    nb: int
+    window_t: int
+    row_ptr: torch.Tensor
+    col_idx: torch.Tensor
+    capacity: int
+
+    def c_index(self) -> VsaIndex:
+        return VsaIndex(self.shape, self.nb, self.window_t, ctypes.c_void_p(self.row_ptr.data_ptr()),
+                        ctypes.c_void_p(self.col_idx.data_ptr()), self.capacity)
+
+    @property
+    def grid(self) -> Tuple[int, int, int]:
+        return (self.shape.T, self.shape.H, self.shape.W)
+
+    @property
+    def block(self) -> Tuple[int, int, int]:
+        return (self.shape.bt, self.shape.bh, self.shape.bw)
+
+    def nnz(self) -> int:
+        return int(self.row_ptr[-1].item())
+
+
+def query(shape: VsaShape, density, window_t: int = -1):
+    """(row_ptr_len, col_capacity, plan_ws_bytes, attn_ws_bytes)."""
+    lib = load()
+    dens, nd = _densities(density, shape.heads)
+    rl, cap = ctypes.c_int64(), ctypes.c_int64()
+    pws, aws = ctypes.c_size_t(), ctypes.c_size_t()
+    check(lib.vsa_query(ctypes.byref(shape), dens, nd, int(window_t), ctypes.byref(rl),
+                        ctypes.byref(cap), ctypes.byref(pws), ctypes.byref(aws)), "vsa_query")
+    return rl.value, cap.value, pws.value, aws.value
+
+
+def plan(q: torch.Tensor, k: torch.Tensor, grid, block, density: Union[float, Sequence[float]],
+         window_t: int = -1) -> Index:
+    """Block means -> centroid scores -> per-row top-k (+ window) -> CSR."""
+    lib = load()
+    shape = _shape_of(q, grid, block)
+    if k.shape != q.shape or k.dtype != q.dtype or not k.is_contiguous():
+        raise ValueError("k must match q")
+    rl, cap, pws, _ = query(shape, density, window_t)
+    dev = q.device
+    row_ptr = torch.empty(rl, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(pws, 1), dtype=torch.uint8, device=dev)
+    cidx = VsaIndex(shape, 0, 0, ctypes.c_void_p(row_ptr.data_ptr()),
+                    ctypes.c_void_p(col_idx.data_ptr()), cap)
+    dens, nd = _densities(density, shape.heads)
+    check(lib.vsa_plan(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                       ctypes.byref(shape), dens, nd, int(window_t), ctypes.byref(cidx),
+                       ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(q)), "vsa_plan")
+    return Index(cidx.shape, cidx.nb, cidx.window_t, row_ptr, col_idx, cap)
+
+
+def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: Index,
+         scale: Optional[float] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Block-sparse attention over the kept blocks; output in raster order."""
+    lib = load()
+    shape = _shape_of(q, index.grid, index.block)
+    for t in (k, v):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("q, k, v must share shape, dtype and be contiguous")
+    if (shape.B, shape.heads, shape.D, shape.dtype) != (index.shape.B, index.shape.heads,
+                                                         index.shape.D, index.shape.dtype):
+        raise ValueError("index was planned for another shape")
+    o = torch.empty_like(q) if out is None else out
+    cidx = index.c_index()
+    check(lib.vsa_attn(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                       ctypes.c_void_p(v.data_ptr()), ctypes.byref(cidx),
+                       ctypes.c_float(0.0 if scale is None else float(scale)),
+                       ctypes.c_void_p(o.data_ptr()), None, 0, _stream(q)), "vsa_attn")
+    return o
+
+
+def permute(x: torch.Tensor, grid, block) -> torch.Tensor:
+    """Raster [B, heads, N, D] -> blocked [B, heads, NB, bt*bh*bw, D] (zero pad)."""
+    lib = load()
+    s = _shape_of(x, grid, block)
+    nb = math.prod(-(-int(n) // int(b)) for n, b in zip(grid, block))
+    P = s.bt * s.bh * s.bw
+    xb = torch.empty((s.B, s.heads, nb, P, s.D), dtype=x.dtype, device=x.device)
+    check(lib.vsa_permute(ctypes.c_void_p(x.data_ptr()), ctypes.byref(s),
+                          ctypes.c_void_p(xb.data_ptr()), _stream(x)), "vsa_permute")
+    return xb
+
+
+def unpermute(xb: torch.Tensor, grid, block) -> torch.Tensor:
+    """Blocked [B, heads, NB, P, D] -> raster [B, heads, N, D]."""
+    lib = load()
+    B, Hh, nb, P, D = xb.shape
+    N = math.prod(int(a) for a in grid)
+    x = torch.empty((B, Hh, N, D), dtype=xb.dtype, device=xb.device)
+    s = _shape_of(x, grid, block)
+    if not xb.is_contiguous() or P != s.bt * s.bh * s.bw:
+        raise ValueError("blocked tensor does not match the block shape")
+    check(lib.vsa_unpermute(ctypes.c_void_p(xb.data_ptr()), ctypes.byref(s),
+                            ctypes.c_void_p(x.data_ptr()), _stream(x)), "vsa_unpermute")
+    return x
+
+
+def centroids(x: torch.Tensor, grid, block) -> torch.Tensor:
+    """Block means in float32 [B, heads, NB, D] (the planning order)."""
+    lib = load()
+    s = _shape_of(x, grid, block)
+    nb = math.prod(-(-int(n) // int(b)) for n, b in zip(grid, block))
+    out = torch.empty((s.B, s.heads, nb, s.D), dtype=torch.float32, device=x.device)
+    check(lib.vsa_centroids(ctypes.c_void_p(x.data_ptr()), ctypes.byref(s),
+                            ctypes.c_void_p(out.data_ptr()), _stream(x)), "vsa_centroids")
+    return out
+
+
+def centroid_scores(qc: torch.Tensor, kc: torch.Tensor, grid, block, dtype=torch.bfloat16) -> torch.Tensor:
+    """Score matrix [B, heads, NB, NB] from float32 block means."""
+    lib = load()
+    B, Hh, nb, D = qc.shape
+    N = math.prod(int(a) for a in grid)
+    s = VsaShape(B, Hh, D, *(int(a) for a in grid), *(int(a) for a in block), _DTYPES[dtype])
+    if qc.dtype != torch.float32 or kc.shape != qc.shape or not qc.is_contiguous() or not kc.is_contiguous():
+        raise ValueError("qc, kc must be contiguous float32 [B, heads, NB, D]")
+    del N
+    out = torch.empty((B, Hh, nb, nb), dtype=torch.float32, device=qc.device)
+    check(lib.vsa_centroid_scores(ctypes.c_void_p(qc.data_ptr()), ctypes.c_void_p(kc.data_ptr()),
+                                  ctypes.byref(s), ctypes.c_void_p(out.data_ptr()), _stream(qc)),
+          "vsa_centroid_scores")
+    return out

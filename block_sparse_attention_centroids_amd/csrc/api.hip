@@ -1,0 +1,183 @@
+// C ABI entry points (declared in include/vsa.h): host validation, then
+// kernel launches on the caller's stream.  No allocation, no device
+// synchronization, no global mutable state.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "vsa.h"
+#include "vsa_host.h"
+#include "vsa_kernels.h"
+
+using namespace vsa;
+
+namespace {
+
+DGeo to_dgeo(const Geo& g) {
+  DGeo d;
+  d.T = g.T; d.H = g.H; d.W = g.W;
+  d.bt = g.bt; d.bh = g.bh; d.bw = g.bw;
+  d.nbt = g.nbt; d.nbh = g.nbh; d.nbw = g.nbw;
+  d.NB = g.NB; d.N = g.N;
+  return d;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool same_shape(const vsa_shape& a, const vsa_shape& b) {
+  return a.B == b.B && a.heads == b.heads && a.D == b.D && a.T == b.T && a.H == b.H &&
+         a.W == b.W && a.bt == b.bt && a.bh == b.bh && a.bw == b.bw && a.dtype == b.dtype;
+}
+
+vsa_status hip_status(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* vsa_status_str(vsa_status s) {
+  switch (s) {
+    case VSA_OK: return "ok";
+    case VSA_ERR_INVALID_ARG: return "invalid argument";
+    case VSA_ERR_UNSUPPORTED: return "unsupported shape or size";
+    case VSA_ERR_WORKSPACE: return "workspace too small";
+    case VSA_ERR_CAPACITY: return "index capacity too small";
+    case VSA_ERR_SHAPE_MISMATCH: return "index does not match the shape";
+    case VSA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+vsa_status vsa_query(const vsa_shape* shape, const float* density, int n_density, int window_t,
+                     int64_t* row_ptr_len, int64_t* col_capacity, size_t* plan_ws, size_t* attn_ws) {
+  try {
+    PlanSizes ps;
+    vsa_status st = plan_sizes(shape, density, n_density, window_t, &ps);
+    if (st != VSA_OK) return st;
+    if (row_ptr_len) *row_ptr_len = ps.rows + 1;
+    if (col_capacity) *col_capacity = ps.capacity;
+    if (plan_ws) *plan_ws = ps.ws;
+    if (attn_ws) *attn_ws = 0;
+    return VSA_OK;
+  } catch (...) {
+    return VSA_ERR_INVALID_ARG;
+  }
+}
+
+vsa_status vsa_plan(const void* q, const void* k, const vsa_shape* shape, const float* density,
+                    int n_density, int window_t, vsa_index* index, void* ws, size_t ws_bytes,
+                    void* stream) {
+  try {
+    if (!q || !k || !index || !ws) return VSA_ERR_INVALID_ARG;
+    PlanSizes ps;
+    vsa_status st = plan_sizes(shape, density, n_density, window_t, &ps);
+    if (st != VSA_OK) return st;
+    if (!index->row_ptr || !index->col_idx) return VSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(ws)) return VSA_ERR_INVALID_ARG;
+    if (index->capacity < ps.capacity) return VSA_ERR_CAPACITY;
+    if (ws_bytes < ps.ws) return VSA_ERR_WORKSPACE;
+    const Geo g = make_geo(*shape);
+    const DGeo dg = to_dgeo(g);
+    const int BH = shape->B * shape->heads;
+    hipStream_t st_ = reinterpret_cast<hipStream_t>(stream);
+    char* w = static_cast<char*>(ws);
+    float* qc = reinterpret_cast<float*>(w + ps.off_qc);
+    float* kc = reinterpret_cast<float*>(w + ps.off_kc);
+
+    SelectArgs sa;
+    std::memset(&sa, 0, sizeof(sa));
+    int64_t sumk = 0;
+    for (int h = 0; h < shape->heads; ++h) {
+      sa.k[h] = ps.k[h];
+      sa.off[h] = static_cast<int32_t>(sumk);
+      sumk += ps.k[h];
+    }
+    sa.batch_stride = sumk * g.NB;
+    sa.rows = ps.rows;
+    sa.window_t = window_t;
+    sa.words = ps.words;
+    int32_t* counts = window_t >= 0 ? reinterpret_cast<int32_t*>(w + ps.off_cnt) : nullptr;
+    uint64_t* bits = window_t >= 0 ? reinterpret_cast<uint64_t*>(w + ps.off_bits) : nullptr;
+
+    index->shape = *shape;
+    index->nb = g.NB;
+    index->window_t = window_t;
+
+    hipError_t e = launch_pool(q, shape->dtype, shape->D, qc, dg, BH, st_);
+    if (e == hipSuccess) e = launch_pool(k, shape->dtype, shape->D, kc, dg, BH, st_);
+    if (e == hipSuccess)
+      e = launch_score_select(qc, kc, dg, shape->D, shape->heads, BH, sa, index->row_ptr,
+                              index->col_idx, counts, bits, st_);
+    if (e == hipSuccess && window_t >= 0)
+      e = launch_scan_fill(counts, bits, index->row_ptr, index->col_idx, ps.rows, ps.words, g.NB,
+                           index->capacity, st_);
+    return hip_status(e);
+  } catch (...) {
+    return VSA_ERR_INVALID_ARG;
+  }
+}
+
+vsa_status vsa_attn(const void* q, const void* k, const void* v, const vsa_index* index,
+                    float scale, void* o, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!q || !k || !v || !o || !index) return VSA_ERR_INVALID_ARG;
+  if (!index->row_ptr || !index->col_idx) return VSA_ERR_INVALID_ARG;
+  vsa_status st = check_shape(&index->shape);
+  if (st != VSA_OK) return st;
+  const Geo g = make_geo(index->shape);
+  if (index->nb != g.NB || index->window_t < -1) return VSA_ERR_SHAPE_MISMATCH;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return VSA_ERR_INVALID_ARG;
+  if (scale == 0.0f) scale = 1.0f / std::sqrt(static_cast<float>(index->shape.D));
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return VSA_ERR_INVALID_ARG;
+  const int BH = index->shape.B * index->shape.heads;
+  hipError_t e = launch_attn(q, k, v, o, index->shape.dtype, index->shape.D, index->row_ptr,
+                             index->col_idx, to_dgeo(g), BH, scale,
+                             reinterpret_cast<hipStream_t>(stream));
+  return hip_status(e);
+}
+
+vsa_status vsa_permute(const void* x, const vsa_shape* shape, void* xb, void* stream) {
+  vsa_status st = check_shape(shape);
+  if (st != VSA_OK) return st;
+  if (!x || !xb || !aligned16(x) || !aligned16(xb)) return VSA_ERR_INVALID_ARG;
+  const Geo g = make_geo(*shape);
+  const int P = shape->bt * shape->bh * shape->bw;
+  return hip_status(launch_permute(x, xb, elt_bytes(shape->dtype), shape->D, to_dgeo(g),
+                                   shape->B * shape->heads, P, false,
+                                   reinterpret_cast<hipStream_t>(stream)));
+}
+
+vsa_status vsa_unpermute(const void* xb, const vsa_shape* shape, void* x, void* stream) {
+  vsa_status st = check_shape(shape);
+  if (st != VSA_OK) return st;
+  if (!x || !xb || !aligned16(x) || !aligned16(xb)) return VSA_ERR_INVALID_ARG;
+  const Geo g = make_geo(*shape);
+  const int P = shape->bt * shape->bh * shape->bw;
+  return hip_status(launch_permute(x, const_cast<void*>(xb), elt_bytes(shape->dtype), shape->D,
+                                   to_dgeo(g), shape->B * shape->heads, P, true,
+                                   reinterpret_cast<hipStream_t>(stream)));
+}
+
+vsa_status vsa_centroids(const void* x, const vsa_shape* shape, float* out, void* stream) {
+  vsa_status st = check_shape(shape);
+  if (st != VSA_OK) return st;
+  if (!x || !out || !aligned16(x) || !aligned16(out)) return VSA_ERR_INVALID_ARG;
+  const Geo g = make_geo(*shape);
+  return hip_status(launch_pool(x, shape->dtype, shape->D, out, to_dgeo(g), shape->B * shape->heads,
+                                reinterpret_cast<hipStream_t>(stream)));
+}
+
+vsa_status vsa_centroid_scores(const float* qc, const float* kc, const vsa_shape* shape, float* out,
+                               void* stream) {
+  vsa_status st = check_shape(shape);
+  if (st != VSA_OK) return st;
+  if (!qc || !kc || !out || !aligned16(qc) || !aligned16(kc)) return VSA_ERR_INVALID_ARG;
+  const Geo g = make_geo(*shape);
+  return hip_status(launch_scores(qc, kc, out, g.NB, shape->D, shape->B * shape->heads,
+                                  reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

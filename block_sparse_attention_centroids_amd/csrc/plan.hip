@@ -1,0 +1,331 @@
+// Planning kernels for gfx950: block means (the summarizer), centroid dot
+// products (the inter-estimator) with per-row top-k selection and the local
+// temporal window, and the CSR scan/fill used when rows vary in length.
+// SPADE (arXiv 2608.03335) 3.1 Fig. 4(c) and 3.3.
+//
+// This file is built with -ffp-contract=off and every product/sum uses the
+// explicitly rounded intrinsics, so the arithmetic is the fixed float32
+// order that makes the index reproducible bit for bit:
+//   mean  = (((+0 + x_0) + x_1) + ... + x_{n-1}) / n
+//   score = ((+0 + q_0*k_0) + q_1*k_1) + ... + q_{D-1}*k_{D-1}
+#include <hip/hip_runtime.h>
+
+#include "vsa_device.h"
+#include "vsa_kernels.h"
+
+#pragma clang fp contract(off)
+
+namespace vsa {
+
+// ---------------------------------------------------------------------------
+// Block means.  One wave per (tensor row bh, block j); lane c owns D/64
+// consecutive channels and walks the block's tokens in block order.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ x, float* __restrict__ out,
+                                                   DGeo g, int nitems) {
+  constexpr int C = D / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + wave;
+  if (item >= nitems) return;
+  const int bh = item / g.NB, j = item - bh * g.NB;
+  const Box b = block_box(g, j);
+  const T* xb = x + (size_t)bh * g.N * D + lane * C;
+  float acc[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) acc[c] = 0.0f;
+  for (int ut = 0; ut < b.et; ++ut) {
+    for (int uh = 0; uh < b.eh; ++uh) {
+      const int row0 = ((b.t0 + ut) * g.H + (b.h0 + uh)) * g.W + b.w0;
+      const T* p = xb + (size_t)row0 * D;
+      int uw = 0;
+      // Loads are issued ahead in groups of 8; the adds stay in token order.
+      for (; uw + 8 <= b.ew; uw += 8) {
+        float v[8][C];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if constexpr (sizeof(T) == 2) {
+            if constexpr (C == 2) {
+              uint32_t two = *reinterpret_cast<const uint32_t*>(p + (size_t)(uw + e) * D);
+              v[e][0] = bf16_lo(two);
+              v[e][1] = bf16_hi(two);
+            } else {
+              v[e][0] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(p + (size_t)(uw + e) * D));
+            }
+          } else {
+#pragma unroll
+            for (int c = 0; c < C; ++c) v[e][c] = reinterpret_cast<const float*>(p)[(size_t)(uw + e) * D + c];
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+          for (int c = 0; c < C; ++c) acc[c] = __fadd_rn(acc[c], v[e][c]);
+      }
+      for (; uw < b.ew; ++uw) {
+        float v[C];
+        if constexpr (sizeof(T) == 2) {
+          if constexpr (C == 2) {
+            uint32_t two = *reinterpret_cast<const uint32_t*>(p + (size_t)uw * D);
+            v[0] = bf16_lo(two);
+            v[1] = bf16_hi(two);
+          } else {
+            v[0] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(p + (size_t)uw * D));
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < C; ++c) v[c] = reinterpret_cast<const float*>(p)[(size_t)uw * D + c];
+        }
+#pragma unroll
+        for (int c = 0; c < C; ++c) acc[c] = __fadd_rn(acc[c], v[c]);
+      }
+    }
+  }
+  const float n = (float)b.n();
+  float* o = out + (size_t)item * D + lane * C;
+#pragma unroll
+  for (int c = 0; c < C; ++c) o[c] = __fdiv_rn(acc[c], n);
+}
+
+// Scores of RT query blocks (rows i0..i0+RT-1, clamped) against key block j.
+// The query means are wave-uniform, so they come through scalar loads.
+template <int RT>
+__device__ inline void score_column(const float* __restrict__ qrows, const float* __restrict__ kj,
+                                    int D, float (&acc)[RT]) {
+#pragma unroll
+  for (int r = 0; r < RT; ++r) acc[r] = 0.0f;
+  for (int d = 0; d < D; d += 4) {
+    const float4 kv = *reinterpret_cast<const float4*>(kj + d);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const float4 qv = *reinterpret_cast<const float4*>(qrows + (size_t)r * D + d);
+      acc[r] = __fadd_rn(acc[r], __fmul_rn(qv.x, kv.x));
+      acc[r] = __fadd_rn(acc[r], __fmul_rn(qv.y, kv.y));
+      acc[r] = __fadd_rn(acc[r], __fmul_rn(qv.z, kv.z));
+      acc[r] = __fadd_rn(acc[r], __fmul_rn(qv.w, kv.w));
+    }
+  }
+}
+
+// Orderable key of a score: larger float -> larger key; -0 and +0 map to
+// the same key, so they tie (and the lower block id wins).
+__device__ inline uint32_t order_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if ((u << 1) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------------------
+// Scores + selection.  One workgroup per (bh, tile of RT query blocks).
+// Phase 1 fills LDS with the RT x NB score rows; phase 2 gives each wave a
+// row: the k-th largest key is found bit by bit from the top (a count of
+// keys >= candidate per bit), then the row is emitted in ascending block id
+// with ties at the threshold going to the lowest ids.
+// ---------------------------------------------------------------------------
+template <int RT>
+__global__ __launch_bounds__(256) void score_select_kernel(
+    const float* __restrict__ qc, const float* __restrict__ kc, DGeo g, int D, int heads,
+    SelectArgs sa, int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
+    int32_t* __restrict__ counts, uint64_t* __restrict__ bits) {
+  extern __shared__ uint32_t smem[];   // [RT][NB] keys
+  const int NB = g.NB;
+  const int bh = blockIdx.y;
+  const int i0 = blockIdx.x * RT;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int rows_here = min(RT, NB - i0);
+  // Phase 1: scores.  Rows past NB reuse the last valid row (never emitted).
+  const float* kbase = kc + (size_t)bh * NB * D;
+  if (rows_here == RT) {
+    for (int j = tid; j < NB; j += 256) {
+      float acc[RT];
+      score_column<RT>(qc + ((size_t)bh * NB + i0) * D, kbase + (size_t)j * D, D, acc);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) smem[r * NB + j] = order_key(acc[r]);
+    }
+  } else {
+    for (int j = tid; j < NB; j += 256) {
+      for (int r = 0; r < rows_here; ++r) {
+        float acc[1];
+        score_column<1>(qc + ((size_t)bh * NB + i0 + r) * D, kbase + (size_t)j * D, D, acc);
+        smem[r * NB + j] = order_key(acc[0]);
+      }
+    }
+  }
+  __syncthreads();
+
+  // Phase 2: selection, one wave per row.
+  const int h = bh % heads;
+  const int b = bh / heads;
+  const int kk = sa.k[h];
+  const int per_t = g.nbh * g.nbw;
+  for (int r = wave; r < rows_here; r += 4) {
+    const int i = i0 + r;
+    const uint32_t* keys = smem + r * NB;
+    uint32_t thr = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = thr | (1u << bit);
+      int cnt = 0;
+      for (int j = lane; j < NB; j += 64) cnt += keys[j] >= cand ? 1 : 0;
+      cnt = wave_sum(cnt);
+      if (cnt >= kk) thr = cand;
+    }
+    int gt = 0;
+    for (int j = lane; j < NB; j += 64) gt += keys[j] > thr ? 1 : 0;
+    gt = wave_sum(gt);
+    const int need = kk - gt;   // >= 1 keys equal to thr are kept, lowest ids first
+    const int tbi = i / per_t;
+    const int64_t row = (int64_t)bh * NB + i;
+    const int64_t out0 = (int64_t)b * sa.batch_stride + (int64_t)NB * sa.off[h] + (int64_t)i * kk;
+    int eq_before = 0, base = 0;
+    const uint64_t lt = lanemask_lt();
+    for (int s = 0; s * 64 < NB; ++s) {
+      const int j = s * 64 + lane;
+      const bool valid = j < NB;
+      const uint32_t key = valid ? keys[j] : 0u;
+      const bool eq = valid && key == thr;
+      const uint64_t eqm = __ballot(eq);
+      const int rank_eq = eq_before + __popcll(eqm & lt);
+      bool keep = valid && (key > thr || (eq && rank_eq < need));
+      if (sa.window_t >= 0 && valid) {
+        const int dt = j / per_t - tbi;
+        keep = keep || (dt <= sa.window_t && -dt <= sa.window_t);
+      }
+      const uint64_t km = __ballot(keep);
+      if (sa.window_t >= 0) {
+        if (lane == 0) bits[row * sa.words + s] = km;
+      } else if (keep) {
+        const int pos = base + __popcll(km & lt);
+        if (pos < kk) col_idx[out0 + pos] = j;
+      }
+      base += __popcll(km);
+      eq_before += __popcll(eqm);
+    }
+    if (lane == 0) {
+      if (sa.window_t >= 0) {
+        counts[row] = base;
+      } else {
+        row_ptr[row] = (int32_t)out0;
+        if (row == sa.rows - 1) row_ptr[row + 1] = (int32_t)(out0 + kk);
+      }
+    }
+  }
+}
+
+// Exclusive scan of per-row counts into row_ptr (one workgroup).
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ row_ptr, int64_t R) {
+  __shared__ int64_t part[1024];
+  const int t = threadIdx.x;
+  const int64_t chunk = (R + 1023) / 1024;
+  const int64_t lo = min<int64_t>(R, (int64_t)t * chunk), hi = min<int64_t>(R, lo + chunk);
+  int64_t s = 0;
+  for (int64_t r = lo; r < hi; ++r) s += counts[r];
+  part[t] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    int64_t v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int64_t run = part[t] - s;   // exclusive prefix of this thread's chunk
+  for (int64_t r = lo; r < hi; ++r) {
+    row_ptr[r] = (int32_t)run;
+    run += counts[r];
+  }
+  if (t == 1023) row_ptr[R] = (int32_t)part[1023];
+}
+
+// Bitmap rows -> ascending column lists at row_ptr (one wave per row).
+__global__ __launch_bounds__(256) void fill_kernel(const uint64_t* __restrict__ bits,
+                                                   const int32_t* __restrict__ row_ptr,
+                                                   int32_t* __restrict__ col_idx, int64_t R, int words,
+                                                   int NB, int64_t capacity) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= R) return;
+  int64_t base = row_ptr[row];
+  const uint64_t lt = lanemask_lt();
+  for (int s = 0; s < words; ++s) {
+    const uint64_t w = bits[row * words + s];
+    const int j = s * 64 + lane;
+    const int64_t pos = base + __popcll(w & lt);
+    if (j < NB && ((w >> lane) & 1ull) && pos < capacity) col_idx[pos] = j;
+    base += __popcll(w);
+  }
+}
+
+// Full score matrix (the inter-estimator alone), same order as above.
+__global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ qc,
+                                                     const float* __restrict__ kc,
+                                                     float* __restrict__ out, int NB, int D) {
+  const int bh = blockIdx.y;
+  const int i = blockIdx.x;
+  for (int j = threadIdx.x; j < NB; j += 256) {
+    float acc[1];
+    score_column<1>(qc + ((size_t)bh * NB + i) * D, kc + ((size_t)bh * NB + j) * D, D, acc);
+    out[((size_t)bh * NB + i) * NB + j] = acc[0];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_pool(const void* x, int dtype, int D, float* out, const DGeo& g, int BH,
+                       hipStream_t st) {
+  const int nitems = BH * g.NB;
+  dim3 grid((nitems + 3) / 4), block(256);
+  if (dtype == 0) {
+    if (D == 128)
+      hipLaunchKernelGGL((pool_kernel<uint16_t, 128>), grid, block, 0, st, (const uint16_t*)x, out, g, nitems);
+    else
+      hipLaunchKernelGGL((pool_kernel<uint16_t, 64>), grid, block, 0, st, (const uint16_t*)x, out, g, nitems);
+  } else {
+    if (D == 128)
+      hipLaunchKernelGGL((pool_kernel<float, 128>), grid, block, 0, st, (const float*)x, out, g, nitems);
+    else
+      hipLaunchKernelGGL((pool_kernel<float, 64>), grid, block, 0, st, (const float*)x, out, g, nitems);
+  }
+  return hipGetLastError();
+}
+
+int select_rows_per_block(int NB) {
+  // RT rows of NB uint32 keys must fit in 64 KiB of LDS.
+  if (NB * 8 * 4 <= 65536) return 8;
+  if (NB * 4 * 4 <= 65536) return 4;
+  if (NB * 2 * 4 <= 65536) return 2;
+  return 1;
+}
+
+hipError_t launch_score_select(const float* qc, const float* kc, const DGeo& g, int D, int heads,
+                               int BH, const SelectArgs& sa, int32_t* row_ptr, int32_t* col_idx,
+                               int32_t* counts, uint64_t* bits, hipStream_t st) {
+  const int RT = select_rows_per_block(g.NB);
+  dim3 grid((g.NB + RT - 1) / RT, BH), block(256);
+  size_t lds = (size_t)RT * g.NB * sizeof(uint32_t);
+  switch (RT) {
+    case 8: hipLaunchKernelGGL(score_select_kernel<8>, grid, block, lds, st, qc, kc, g, D, heads, sa, row_ptr, col_idx, counts, bits); break;
+    case 4: hipLaunchKernelGGL(score_select_kernel<4>, grid, block, lds, st, qc, kc, g, D, heads, sa, row_ptr, col_idx, counts, bits); break;
+    case 2: hipLaunchKernelGGL(score_select_kernel<2>, grid, block, lds, st, qc, kc, g, D, heads, sa, row_ptr, col_idx, counts, bits); break;
+    default: hipLaunchKernelGGL(score_select_kernel<1>, grid, block, lds, st, qc, kc, g, D, heads, sa, row_ptr, col_idx, counts, bits); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_fill(const int32_t* counts, const uint64_t* bits, int32_t* row_ptr,
+                            int32_t* col_idx, int64_t R, int words, int NB, int64_t capacity,
+                            hipStream_t st) {
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, row_ptr, R);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, st, bits, row_ptr, col_idx, R, words, NB, capacity);
+  return hipGetLastError();
+}
+
+hipError_t launch_scores(const float* qc, const float* kc, float* out, int NB, int D, int BH,
+                         hipStream_t st) {
+  hipLaunchKernelGGL(scores_kernel, dim3(NB, BH), dim3(256), 0, st, qc, kc, out, NB, D);
+  return hipGetLastError();
+}
+
+}  // namespace vsa

@@ -1,0 +1,143 @@
+// Host-side geometry, keep-rate rule, validation and workspace layout.
+// Pure C++ (no HIP): everything here runs before any launch.
+#pragma once
+
+#include <algorithm>
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "vsa.h"
+
+namespace vsa {
+
+struct Geo {
+  int T, H, W;
+  int bt, bh, bw;
+  int nbt, nbh, nbw;
+  int NB;
+  int N;
+};
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline Geo make_geo(const vsa_shape& s) {
+  Geo g;
+  g.T = s.T; g.H = s.H; g.W = s.W;
+  g.bt = s.bt; g.bh = s.bh; g.bw = s.bw;
+  g.nbt = ceil_div(s.T, s.bt);
+  g.nbh = ceil_div(s.H, s.bh);
+  g.nbw = ceil_div(s.W, s.bw);
+  g.NB = g.nbt * g.nbh * g.nbw;
+  g.N = s.T * s.H * s.W;
+  return g;
+}
+
+// Tokens in block j: product of its (possibly cut-short) extents.
+inline int block_tokens(const Geo& g, int j) {
+  int tb = j / (g.nbh * g.nbw), r = j % (g.nbh * g.nbw);
+  int hb = r / g.nbw, wb = r % g.nbw;
+  int et = std::min(g.bt, g.T - tb * g.bt);
+  int eh = std::min(g.bh, g.H - hb * g.bh);
+  int ew = std::min(g.bw, g.W - wb * g.bw);
+  return et * eh * ew;
+}
+
+// Keep-rate rule: k = min(NB, max(1, floor(density*NB + 0.5))), in double
+// from the float32 density.
+inline int k_rule(float density, int NB) {
+  double k = std::floor(static_cast<double>(density) * NB + 0.5);
+  if (k < 1) k = 1;
+  if (k > NB) k = NB;
+  return static_cast<int>(k);
+}
+
+// Number of key blocks within +-window_t temporal blocks of a query block in
+// temporal block tb.
+inline int window_count(const Geo& g, int tb, int window_t) {
+  if (window_t < 0) return 0;
+  int lo = std::max(0, tb - window_t), hi = std::min(g.nbt - 1, tb + window_t);
+  return (hi - lo + 1) * g.nbh * g.nbw;
+}
+
+inline int elt_bytes(int dtype) { return dtype == VSA_F32 ? 4 : 2; }
+
+// Shape validation shared by every entry point.
+inline vsa_status check_shape(const vsa_shape* s) {
+  if (!s) return VSA_ERR_INVALID_ARG;
+  if (s->B < 1 || s->heads < 1 || s->D < 1 || s->T < 1 || s->H < 1 || s->W < 1 ||
+      s->bt < 1 || s->bh < 1 || s->bw < 1)
+    return VSA_ERR_INVALID_ARG;
+  if (s->dtype != VSA_BF16 && s->dtype != VSA_F32) return VSA_ERR_INVALID_ARG;
+  if (s->D != 64 && s->D != 128) return VSA_ERR_UNSUPPORTED;
+  // Block box larger than the grid is allowed (it is cut short).
+  int64_t box = int64_t(s->bt) * s->bh * s->bw;
+  int64_t bt = std::min(s->bt, s->T), bh = std::min(s->bh, s->H), bw = std::min(s->bw, s->W);
+  if (bt * bh * bw > VSA_MAX_BLOCK_TOKENS) return VSA_ERR_UNSUPPORTED;
+  (void)box;
+  int64_t N = int64_t(s->T) * s->H * s->W;
+  if (N > (int64_t(1) << 30)) return VSA_ERR_UNSUPPORTED;
+  int64_t elems = int64_t(s->B) * s->heads * N * s->D;
+  if (elems > (int64_t(1) << 40)) return VSA_ERR_UNSUPPORTED;
+  Geo g = make_geo(*s);
+  if (g.NB > 16384) return VSA_ERR_UNSUPPORTED;
+  if (int64_t(s->B) * s->heads * g.NB >= (int64_t(1) << 31) - 1) return VSA_ERR_UNSUPPORTED;
+  return VSA_OK;
+}
+
+struct PlanSizes {
+  int64_t rows = 0;          // B*heads*NB
+  int64_t capacity = 0;      // col_idx entries needed (upper bound with a window)
+  size_t ws = 0;             // plan workspace bytes
+  size_t off_qc = 0, off_kc = 0, off_cnt = 0, off_bits = 0;
+  int words = 0;             // 64-bit bitmap words per row (window mode)
+  std::vector<int> k;        // per head
+};
+
+inline vsa_status plan_sizes(const vsa_shape* s, const float* density, int n_density,
+                             int window_t, PlanSizes* out) {
+  vsa_status st = check_shape(s);
+  if (st != VSA_OK) return st;
+  if (!density || !out) return VSA_ERR_INVALID_ARG;
+  if (n_density != 1 && n_density != s->heads) return VSA_ERR_INVALID_ARG;
+  if (window_t < -1) return VSA_ERR_INVALID_ARG;
+  if (s->heads > VSA_MAX_HEADS) return VSA_ERR_UNSUPPORTED;
+  Geo g = make_geo(*s);
+  out->k.assign(s->heads, 0);
+  for (int h = 0; h < s->heads; ++h) {
+    float d = density[n_density == 1 ? 0 : h];
+    if (!(d > 0.0f) || !(d <= 1.0f)) return VSA_ERR_INVALID_ARG;  // also rejects NaN
+    out->k[h] = k_rule(d, g.NB);
+  }
+  out->rows = int64_t(s->B) * s->heads * g.NB;
+  int64_t cap = 0;
+  for (int h = 0; h < s->heads; ++h) {
+    int64_t per_head = 0;
+    for (int i = 0; i < g.NB; ++i) {
+      int tb = i / (g.nbh * g.nbw);
+      int64_t c = out->k[h] + window_count(g, tb, window_t);
+      per_head += std::min<int64_t>(c, g.NB);
+    }
+    cap += per_head;
+  }
+  cap *= s->B;
+  if (cap >= (int64_t(1) << 31) - 1) return VSA_ERR_UNSUPPORTED;
+  out->capacity = cap;
+  size_t cent = size_t(out->rows) * s->D * sizeof(float);
+  out->off_qc = 0;
+  out->off_kc = align256(cent);
+  size_t ws = out->off_kc + align256(cent);
+  out->words = (g.NB + 63) / 64;
+  if (window_t >= 0) {
+    out->off_cnt = ws;
+    ws += align256(size_t(out->rows + 1) * sizeof(int32_t));
+    out->off_bits = ws;
+    ws += align256(size_t(out->rows) * out->words * sizeof(uint64_t));
+  }
+  out->ws = ws;
+  return VSA_OK;
+}
+
+}  // namespace vsa

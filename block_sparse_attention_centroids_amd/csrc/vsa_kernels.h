@@ -1,0 +1,38 @@
+// Kernel launchers of the gfx950 library (host-callable, enqueue only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "vsa.h"
+#include "vsa_device.h"
+
+namespace vsa {
+
+// Per-head selection parameters, passed by value as a kernel argument.
+struct SelectArgs {
+  int32_t k[VSA_MAX_HEADS];     // kept blocks per query-block row of head h
+  int32_t off[VSA_MAX_HEADS];   // sum of k over heads before h
+  int64_t batch_stride;         // NB * sum_h k_h: col_idx entries per batch item
+  int64_t rows;                 // B * heads * NB
+  int32_t window_t;             // -1: none
+  int32_t words;                // 64-bit bitmap words per row
+};
+
+hipError_t launch_pool(const void* x, int dtype, int D, float* out, const DGeo& g, int BH,
+                       hipStream_t st);
+hipError_t launch_score_select(const float* qc, const float* kc, const DGeo& g, int D, int heads,
+                               int BH, const SelectArgs& sa, int32_t* row_ptr, int32_t* col_idx,
+                               int32_t* counts, uint64_t* bits, hipStream_t st);
+hipError_t launch_scan_fill(const int32_t* counts, const uint64_t* bits, int32_t* row_ptr,
+                            int32_t* col_idx, int64_t R, int words, int NB, int64_t capacity,
+                            hipStream_t st);
+hipError_t launch_scores(const float* qc, const float* kc, float* out, int NB, int D, int BH,
+                         hipStream_t st);
+hipError_t launch_attn(const void* q, const void* k, const void* v, void* o, int dtype, int D,
+                       const int32_t* row_ptr, const int32_t* col_idx, const DGeo& g, int BH,
+                       float scale, hipStream_t st);
+hipError_t launch_permute(const void* x, void* xb, int elt, int D, const DGeo& g, int BH, int P,
+                          bool inverse, hipStream_t st);
+
+}  // namespace vsa

@@ -1,0 +1,148 @@
+/*
+ * vsa.h -- C ABI of the MI355X (gfx950) library for centroid-scored 3D
+ * block-sparse self-attention over a video latent.
+ *
+ * What the library computes (SPADE: An Input-Adaptive Sparse Attention
+ * Engine for Fast Video Diffusion Models Inference, sections 2.1, 2.2 and
+ * 3.1-3.3):
+ *   1. the T x H x W token grid (flattened in raster order, 2.1) is cut into
+ *      bt x bh x bw boxes (3.1, Fig. 3);
+ *   2. Q and K are summarized per block by their mean (MEAN-SPADE, Fig. 4(c));
+ *   3. the dot products of the means give an N_Qblocks x N_Kblocks importance
+ *      matrix; each query-block row keeps its top-k key blocks (3.3), with k
+ *      from a keep rate, i.e. the share of key blocks retained per query
+ *      block (JEV sparse comparison page, How this was measured), optionally
+ *      united with a local temporal window (3.3);
+ *   4. attention (Eq. 2) runs over the kept blocks only with an online
+ *      softmax, and the output is restored to raster order (3.3).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout.  q, k, v and o are dense, contiguous [B, heads, N, D] arrays with
+ *   N = T*H*W tokens in raster order n = (t*H + h)*W + w.  All four have the
+ *   same element type (vsa_dtype).  Device pointers must be 16-byte aligned.
+ * Blocks.  nbt = ceil(T/bt), nbh = ceil(H/bh), nbw = ceil(W/bw),
+ *   NB = nbt*nbh*nbw.  Block (tb, hb, wb) has id (tb*nbh + hb)*nbw + wb and
+ *   covers the box [tb*bt, min(T, tb*bt+bt)) x ... ; blocks on the far edge
+ *   of a dimension that bt/bh/bw do not divide are cut short and hold fewer
+ *   tokens.  Tokens inside a block are ordered row-major in (t, h, w).
+ * Ownership.  The caller allocates every buffer (inputs, outputs, index
+ *   arrays, workspace).  The library never allocates, never synchronizes the
+ *   device and keeps no mutable global state; calls on different streams do
+ *   not interfere unless they write the same buffers.
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = null stream).
+ *   Work is only enqueued; results are valid once the caller has
+ *   synchronized with the stream.
+ * Errors.  Arguments are validated on the host before anything is enqueued;
+ *   on error nothing is enqueued and the status says why.  A failed kernel
+ *   launch returns VSA_ERR_HIP.  No C++ exception crosses this boundary.
+ */
+#ifndef VSA_H_
+#define VSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VSA_OK = 0,
+  VSA_ERR_INVALID_ARG = 1,    /* null pointer, non-positive size, density out of (0,1], ... */
+  VSA_ERR_UNSUPPORTED = 2,    /* D not 64/128, more than 128 tokens per block, too many blocks/heads */
+  VSA_ERR_WORKSPACE = 3,      /* ws_bytes smaller than vsa_query reported */
+  VSA_ERR_CAPACITY = 4,       /* index->capacity smaller than vsa_query reported */
+  VSA_ERR_SHAPE_MISMATCH = 5, /* an index used with a shape it was not planned for */
+  VSA_ERR_HIP = 6             /* a HIP launch or runtime call failed */
+} vsa_status;
+
+typedef enum { VSA_BF16 = 0, VSA_F32 = 1 } vsa_dtype;
+
+/* Sizes are tokens (T, H, W: latent grid; bt, bh, bw: block box). */
+typedef struct {
+  int32_t B, heads, D;
+  int32_t T, H, W;
+  int32_t bt, bh, bw;
+  int32_t dtype; /* vsa_dtype */
+} vsa_shape;
+
+/* Block index in CSR form (SPADE 3.3: the binary block mask, stored as a
+ * block-sparse row structure).  Row r = (b*heads + h)*nb + i lists the key
+ * blocks kept by query block i of head (b, h) in ascending id order:
+ * col_idx[row_ptr[r] .. row_ptr[r+1]).  row_ptr[0] = 0.
+ * row_ptr: device int32[B*heads*nb + 1]; col_idx: device int32[capacity].
+ * The caller owns both arrays; vsa_plan fills them and sets shape, nb and
+ * window_t. */
+typedef struct {
+  vsa_shape shape;
+  int32_t nb;
+  int32_t window_t;
+  int32_t* row_ptr;
+  int32_t* col_idx;
+  int64_t capacity;
+} vsa_index;
+
+/* Largest supported head count with per-head densities, and block size. */
+#define VSA_MAX_HEADS 256
+#define VSA_MAX_BLOCK_TOKENS 128
+
+/* Host-only sizing query; touches no device.
+ * density: host float[n_density], n_density = 1 (all heads) or heads; each
+ *   value in (0, 1].  k_h = min(NB, max(1, floor(density_h*NB + 0.5))).
+ * window_t: -1 for none, r >= 0 to also keep every key block whose temporal
+ *   block index is within +-r of the query block's.
+ * Outputs (any may be NULL): row_ptr_len = B*heads*NB + 1; col_capacity =
+ *   an upper bound of the kept entries (exact without a window);
+ *   plan_ws / attn_ws = workspace bytes that vsa_plan / vsa_attn need. */
+vsa_status vsa_query(const vsa_shape* shape, const float* density, int n_density,
+                     int window_t, int64_t* row_ptr_len, int64_t* col_capacity,
+                     size_t* plan_ws, size_t* attn_ws);
+
+/* Planning (SPADE 3.3: summarizer, inter-estimator, Top-K, union with the
+ * local window).  q, k: device [B, heads, N, D] of shape->dtype.  Block
+ * means and their dot products are computed in float32 in a fixed order:
+ * mean = (sum over the block's tokens in block order, from +0) / n, and
+ * score = sum over channels in order of separately rounded products, so the
+ * index is reproducible bit for bit.  Ties between equal scores keep the
+ * lower block id.  index: row_ptr, col_idx and capacity set by the caller;
+ * ws: device workspace of at least vsa_query's plan_ws bytes. */
+vsa_status vsa_plan(const void* q, const void* k, const vsa_shape* shape,
+                    const float* density, int n_density, int window_t,
+                    vsa_index* index, void* ws, size_t ws_bytes, void* stream);
+
+/* Block-sparse attention (SPADE 2.2 Eq. 2 with M = 0 on kept block pairs and
+ * -inf elsewhere; 3.3 flash block-sparse attention and layout restore).
+ * q, k, v, o: device [B, heads, N, D] in index->shape; o is written in
+ * raster order.  scale: logit scale, 0 means 1/sqrt(D).  bf16 uses bf16
+ * matrix cores with float32 accumulation and a float32 online softmax; f32
+ * computes in float32.  ws may be NULL when attn_ws is 0. */
+vsa_status vsa_attn(const void* q, const void* k, const void* v, const vsa_index* index,
+                    float scale, void* o, void* ws, size_t ws_bytes, void* stream);
+
+/* Layout transform (SPADE 3.3: Q, K, V rearranged into the blocked layout).
+ * x: device [B, heads, N, D]; xb: device [B, heads, NB, P, D] with
+ * P = bt*bh*bw; rows past a block's token count are written as zero. */
+vsa_status vsa_permute(const void* x, const vsa_shape* shape, void* xb, void* stream);
+
+/* Inverse of vsa_permute (SPADE 3.3: output blocks restored to the original
+ * layout); pad rows of xb are ignored. */
+vsa_status vsa_unpermute(const void* xb, const vsa_shape* shape, void* x, void* stream);
+
+/* Block means alone (the summarizer of vsa_plan, SPADE 3.1 Fig. 4(c)):
+ * x: device [B, heads, N, D]; out: device float32 [B, heads, NB, D]. */
+vsa_status vsa_centroids(const void* x, const vsa_shape* shape, float* out, void* stream);
+
+/* Centroid score matrix alone (the inter-estimator of vsa_plan, SPADE 3.3):
+ * qc, kc: device float32 [B, heads, NB, D]; out: device float32
+ * [B, heads, NB, NB] with out[.., i, j] = <qc_i, kc_j> in vsa_plan's order. */
+vsa_status vsa_centroid_scores(const float* qc, const float* kc, const vsa_shape* shape,
+                               float* out, void* stream);
+
+/* Static description of a status code. */
+const char* vsa_status_str(vsa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VSA_H_ */

@@ -1,0 +1,173 @@
+"""The C ABI on the host: the library loads, exports every function that
+include/vsa.h declares, sizes the index as the oracle's geometry says, and
+rejects bad arguments with the documented status before launching anything.
+No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import workloads as W
+from block_sparse_attention_centroids_amd import _lib
+from block_sparse_attention_centroids_amd._lib import VsaIndex, VsaShape
+from oracle import vsa_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libvsa.so is not built (run python -m block_sparse_attention_centroids_amd.build)")
+    return _lib.load()
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "vsa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(vsa_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert "vsa_plan" in names and "vsa_attn" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert lib.vsa_status_str(s)
+    assert lib.vsa_status_str(0) == b"ok"
+
+
+def _shape(w, dtype=_lib.VSA_BF16):
+    return VsaShape(w.B, w.heads, w.D, *w.grid, *w.block, dtype)
+
+
+def _query(lib, shape, dens, window_t=-1):
+    arr = (ctypes.c_float * len(dens))(*dens)
+    rl, cap = ctypes.c_int64(), ctypes.c_int64()
+    pws, aws = ctypes.c_size_t(), ctypes.c_size_t()
+    st = lib.vsa_query(ctypes.byref(shape), arr, len(dens), window_t, ctypes.byref(rl), ctypes.byref(cap),
+                       ctypes.byref(pws), ctypes.byref(aws))
+    return st, rl.value, cap.value, pws.value, aws.value
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "wan13b", "hunyuan", "wan14b_mixed", "long4x"])
+def test_query_matches_oracle_geometry(lib, name):
+    w = W.WORKLOADS[name]
+    g = O.geometry(w.grid, w.block)
+    dens = [0.20] * w.heads if w.density is None else [w.density]
+    if name == "wan14b_mixed":
+        dens = list(np.random.default_rng(0).choice(W.DENSITY_OPTIONS_MIXED, size=w.heads))
+    st, rl, cap, pws, aws = _query(lib, _shape(w), dens, w.window_t)
+    assert st == 0
+    assert rl == w.B * w.heads * g.NB + 1
+    ks = [O.k_rule(d, g.NB) for d in np.broadcast_to(np.float32(dens), (w.heads,))]
+    if w.window_t < 0:
+        assert cap == w.B * g.NB * sum(ks)
+    else:
+        bound = sum(min(g.NB, ks[h] + len(O.window_blocks(g, i, w.window_t)))
+                    for h in range(w.heads) for i in range(g.NB))
+        assert cap == w.B * bound
+    assert pws >= 2 * w.B * w.heads * g.NB * w.D * 4
+    assert aws == 0
+
+
+def test_query_rejects_bad_arguments(lib):
+    w = W.WORKLOADS["wan13b"]
+    ok = _shape(w)
+    assert _query(lib, ok, [0.2])[0] == 0
+    assert _query(lib, ok, [0.0])[0] == _lib.VSA_ERR_INVALID_ARG
+    assert _query(lib, ok, [1.5])[0] == _lib.VSA_ERR_INVALID_ARG
+    assert _query(lib, ok, [float("nan")])[0] == _lib.VSA_ERR_INVALID_ARG
+    assert _query(lib, ok, [0.2, 0.3])[0] == _lib.VSA_ERR_INVALID_ARG      # neither 1 nor heads
+    assert _query(lib, ok, [0.2], window_t=-2)[0] == _lib.VSA_ERR_INVALID_ARG
+    bad = VsaShape(1, 12, 96, 21, 30, 52, 4, 4, 8, 0)
+    assert _query(lib, bad, [0.2])[0] == _lib.VSA_ERR_UNSUPPORTED           # D = 96
+    bad = VsaShape(1, 12, 128, 21, 30, 52, 8, 8, 8, 0)
+    assert _query(lib, bad, [0.2])[0] == _lib.VSA_ERR_UNSUPPORTED           # 512-token blocks
+    bad = VsaShape(1, 12, 128, 0, 30, 52, 4, 4, 8, 0)
+    assert _query(lib, bad, [0.2])[0] == _lib.VSA_ERR_INVALID_ARG           # empty grid
+    bad = VsaShape(1, 12, 128, 21, 30, 52, 4, 4, 8, 7)
+    assert _query(lib, bad, [0.2])[0] == _lib.VSA_ERR_INVALID_ARG           # unknown dtype
+    bad = VsaShape(1, 300, 128, 21, 30, 52, 4, 4, 8, 0)
+    assert _query(lib, bad, [0.2])[0] == _lib.VSA_ERR_UNSUPPORTED           # too many heads
+    assert lib.vsa_query(None, None, 1, -1, None, None, None, None) == _lib.VSA_ERR_INVALID_ARG
+    # a block box larger than the grid is cut short, not rejected
+    big = VsaShape(1, 1, 64, 2, 3, 5, 4, 4, 8, 1)
+    st, rl, cap, _, _ = _query(lib, big, [1.0])
+    assert st == 0 and rl == 2 and cap == 1
+
+
+FAKE = ctypes.c_void_p(0x100000)   # aligned non-null address; never dereferenced
+
+
+def test_plan_error_paths(lib):
+    w = W.WORKLOADS["wan13b"]
+    shape = _shape(w)
+    st, rl, cap, pws, _ = _query(lib, shape, [0.2])
+    dens = (ctypes.c_float * 1)(0.2)
+
+    def call(q=FAKE, k=FAKE, cap_=cap, ws=FAKE, ws_bytes=pws, d=dens, nd=1, win=-1, rp=FAKE, ci=FAKE):
+        idx = VsaIndex(shape, 0, 0, rp, ci, cap_)
+        return lib.vsa_plan(q, k, ctypes.byref(shape), d, nd, win, ctypes.byref(idx), ws, ws_bytes, None)
+
+    assert call(q=None) == _lib.VSA_ERR_INVALID_ARG
+    assert call(ws=None) == _lib.VSA_ERR_INVALID_ARG
+    assert call(rp=None) == _lib.VSA_ERR_INVALID_ARG
+    assert call(cap_=cap - 1) == _lib.VSA_ERR_CAPACITY
+    assert call(ws_bytes=pws - 1) == _lib.VSA_ERR_WORKSPACE
+    assert call(q=ctypes.c_void_p(0x100008)) == _lib.VSA_ERR_INVALID_ARG   # misaligned
+    assert call(d=(ctypes.c_float * 1)(-1.0)) == _lib.VSA_ERR_INVALID_ARG
+
+
+def test_attn_error_paths(lib):
+    w = W.WORKLOADS["wan13b"]
+    shape = _shape(w)
+    g = O.geometry(w.grid, w.block)
+
+    def call(nb=g.NB, scale=0.0, q=FAKE, win=-1, rp=FAKE):
+        idx = VsaIndex(shape, nb, win, rp, FAKE, 10)
+        return lib.vsa_attn(q, FAKE, FAKE, ctypes.byref(idx), ctypes.c_float(scale), FAKE, None, 0, None)
+
+    assert call(nb=g.NB + 1) == _lib.VSA_ERR_SHAPE_MISMATCH
+    assert call(win=-3) == _lib.VSA_ERR_SHAPE_MISMATCH
+    assert call(scale=-1.0) == _lib.VSA_ERR_INVALID_ARG
+    assert call(scale=float("inf")) == _lib.VSA_ERR_INVALID_ARG
+    assert call(q=None) == _lib.VSA_ERR_INVALID_ARG
+    assert call(rp=None) == _lib.VSA_ERR_INVALID_ARG
+    assert call(q=ctypes.c_void_p(0x100004)) == _lib.VSA_ERR_INVALID_ARG
+
+
+def test_layout_entry_error_paths(lib):
+    bad = VsaShape(1, 1, 96, 4, 8, 8, 2, 4, 8, 0)
+    assert lib.vsa_permute(FAKE, ctypes.byref(bad), FAKE, None) == _lib.VSA_ERR_UNSUPPORTED
+    ok = VsaShape(1, 1, 64, 4, 8, 8, 2, 4, 8, 0)
+    assert lib.vsa_permute(None, ctypes.byref(ok), FAKE, None) == _lib.VSA_ERR_INVALID_ARG
+    assert lib.vsa_unpermute(FAKE, ctypes.byref(ok), None, None) == _lib.VSA_ERR_INVALID_ARG
+    assert lib.vsa_centroids(FAKE, ctypes.byref(ok), None, None) == _lib.VSA_ERR_INVALID_ARG
+    assert lib.vsa_centroid_scores(FAKE, None, ctypes.byref(ok), FAKE, None) == _lib.VSA_ERR_INVALID_ARG
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    import block_sparse_attention_centroids_amd as pkg
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libvsa.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        pkg.load()
+
+
+def test_token_map_division_is_exact():
+    """The kernels split a block-local token index u into (t, h, w) with a
+    float reciprocal: floor((u + 0.5) * fl(1/e)).  Check every case the
+    kernels can meet (u < 128, extents <= 128) in float32."""
+    u = np.arange(128, dtype=np.float32)[:, None]
+    e = np.arange(1, 129, dtype=np.float32)[None, :]
+    inv = (np.float32(1.0) / e).astype(np.float32)
+    q = np.floor(((u + np.float32(0.5)).astype(np.float32) * inv).astype(np.float32))
+    assert np.array_equal(q.astype(np.int64), (np.arange(128)[:, None] // np.arange(1, 129)[None, :]))

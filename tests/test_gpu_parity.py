@@ -1,0 +1,207 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: block indices, centroids and centroid scores bit-exact; bf16 outputs
+within max-abs 2e-2 and mean-abs 2e-3 of the float64 oracle; float32
+outputs within max-abs 1e-4.  Small cases compare every output element;
+the full-size workloads compare the whole index and a seeded sample of
+query blocks (the largest and the smallest blocks always included).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import vsa_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX, BF16_MEAN, F32_MAX = 2e-2, 2e-3, 1e-4
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def vsa():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import block_sparse_attention_centroids_amd as pkg
+    pkg.load()
+    return pkg
+
+
+def _to_dev(a, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to(device="cuda", dtype=dtype).contiguous()
+
+
+def _tdtype(w):
+    return torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+
+def _run(vsa, w, inp):
+    dt = _tdtype(w)
+    q, k, v = (_to_dev(inp[n], dt) for n in ("q", "k", "v"))
+    dens = [float(d) for d in inp["density"]]
+    idx = vsa.plan(q, k, w.grid, w.block, dens, w.window_t)
+    o = vsa.attn(q, k, v, idx)
+    torch.cuda.synchronize()
+    return q, k, v, idx, o
+
+
+def _index_np(idx):
+    rp = idx.row_ptr.cpu().numpy()
+    return rp, idx.col_idx.cpu().numpy()[: int(rp[-1])]
+
+
+def _check_out(w, got, ref):
+    err = np.abs(got.astype(np.float64) - ref)
+    if w.dtype == "bf16":
+        assert err.max() <= BF16_MAX, f"max-abs {err.max():.3e}"
+        assert err.mean() <= BF16_MEAN, f"mean-abs {err.mean():.3e}"
+    else:
+        assert err.max() <= F32_MAX, f"max-abs {err.max():.3e}"
+    return float(err.max()), float(err.mean())
+
+
+SMALL = [
+    W.custom("s_tiny_fp32", 1, 2, 64, (4, 8, 8), (2, 4, 8), "f32", 0.5, -1, "iid"),
+    W.custom("s_tiny_fp32_dense", 1, 2, 64, (4, 8, 8), (2, 4, 8), "f32", 1.0, -1, "iid"),
+    W.custom("s_ragged_fp32_d128", 1, 2, 128, (3, 5, 7), (2, 2, 4), "f32", 0.4, -1, "iid"),
+    W.custom("s_ragged_bf16", 1, 2, 128, (9, 14, 20), (4, 4, 8), "bf16", 0.25, -1, "smooth"),
+    W.custom("s_hy_bf16_d64", 1, 3, 64, (5, 9, 11), (1, 8, 16), "bf16", 0.3, -1, "smooth"),
+    W.custom("s_window_bf16", 1, 2, 128, (12, 8, 8), (4, 4, 8), "bf16", 0.1, 1, "smooth"),
+    W.custom("s_window0_bf16", 1, 1, 128, (10, 9, 9), (2, 4, 4), "bf16", 0.05, 0, "smooth"),
+    W.custom("s_batch2_bf16", 2, 3, 128, (6, 8, 16), (2, 4, 8), "bf16", None, -1, "smooth"),
+    W.custom("s_single_block", 1, 2, 128, (2, 3, 5), (4, 4, 8), "bf16", 1.0, -1, "smooth"),
+    W.custom("s_token_blocks", 1, 1, 128, (4, 4, 4), (1, 1, 1), "bf16", 0.25, -1, "smooth"),
+    W.custom("s_dense_bf16", 1, 2, 128, (4, 8, 16), (2, 4, 8), "bf16", 1.0, -1, "smooth"),
+]
+
+
+def _gen_small(w):
+    inp = W.generate(w, seed=3)
+    if w.density is None:   # per-head mix including dense and very sparse heads
+        inp["density"] = np.array([1.0, 0.3, 0.05][: w.heads], dtype=np.float32)
+    return inp
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_small_full_parity(vsa, w):
+    _say(f"[gpu] small parity {w.name} grid={w.grid} block={w.block} D={w.D} {w.dtype}")
+    inp = _gen_small(w)
+    q, k, v, idx, o = _run(vsa, w, inp)
+    rp, ci, info = O.plan(inp["q"], inp["k"], w.grid, w.block, inp["density"], w.window_t)
+    grp, gci = _index_np(idx)
+    assert np.array_equal(grp, rp), "row_ptr differs"
+    assert np.array_equal(gci, ci), "col_idx differs"
+    # summarizer and inter-estimator alone, bit for bit
+    qc = vsa.centroids(q, w.grid, w.block)
+    kc = vsa.centroids(k, w.grid, w.block)
+    S = vsa.centroid_scores(qc, kc, w.grid, w.block)
+    torch.cuda.synchronize()
+    assert np.array_equal(qc.cpu().numpy().view(np.uint32), info["qc"].view(np.uint32))
+    assert np.array_equal(kc.cpu().numpy().view(np.uint32), info["kc"].view(np.uint32))
+    assert np.array_equal(S.cpu().numpy(), info["S"])
+    ref = O.attention(inp["q"], inp["k"], inp["v"], w.grid, w.block, rp, ci)
+    mx, mean = _check_out(w, o.float().cpu().numpy(), ref)
+    _say(f"[gpu]   ok max-abs {mx:.2e} mean-abs {mean:.2e}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("grid,block", [((9, 14, 20), (4, 4, 8)), ((5, 9, 11), (1, 8, 16)),
+                                        ((3, 3, 3), (2, 2, 2))])
+def test_permute_unpermute(vsa, grid, block, dtype):
+    _say(f"[gpu] permute {grid} {block} {dtype}")
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((2, 2, math.prod(grid), 64)).astype(np.float32)
+    xd = _to_dev(x, dtype)
+    xb = vsa.permute(xd, grid, block)
+    back = vsa.unpermute(xb, grid, block)
+    torch.cuda.synchronize()
+    g = O.geometry(grid, block)
+    ref = O.permute(xd.cpu().float().numpy(), g, pad_to=block[0] * block[1] * block[2])
+    assert np.array_equal(xb.cpu().float().numpy(), ref)
+    assert torch.equal(back, xd)
+
+
+def test_ties_and_constant_v(vsa):
+    """Q == 0 gives all-equal scores (the lowest ids win); V == 1 gives O == 1."""
+    w = W.custom("ties", 1, 2, 128, (8, 8, 16), (2, 4, 8), "bf16", 0.25, -1, "smooth")
+    _say("[gpu] ties / constant V")
+    inp = W.generate(w, seed=4)
+    q = torch.zeros((1, 2, w.N, 128), dtype=torch.bfloat16, device="cuda")
+    k = _to_dev(inp["k"], torch.bfloat16)
+    v = torch.ones_like(q)
+    idx = vsa.plan(q, k, w.grid, w.block, 0.25)
+    o = vsa.attn(_to_dev(inp["q"], torch.bfloat16), k, v, idx)
+    torch.cuda.synchronize()
+    g = O.geometry(w.grid, w.block)
+    kk = O.k_rule(0.25, g.NB)
+    rp, ci = _index_np(idx)
+    assert np.array_equal(ci.reshape(-1, kk), np.tile(np.arange(kk), (2 * g.NB, 1)))
+    assert torch.all(o == 1)
+
+
+def test_run_twice_bitwise(vsa):
+    w = W.custom("det", 1, 2, 128, (9, 14, 20), (4, 4, 8), "bf16", 0.3, 1, "smooth")
+    _say("[gpu] determinism")
+    inp = W.generate(w, seed=5)
+    _, _, _, idx1, o1 = _run(vsa, w, inp)
+    _, _, _, idx2, o2 = _run(vsa, w, inp)
+    assert torch.equal(idx1.row_ptr, idx2.row_ptr)
+    assert torch.equal(idx1.col_idx[: idx1.nnz()], idx2.col_idx[: idx2.nnz()])
+    assert torch.equal(o1, o2)
+
+
+# ---------------------------------------------------------------- full size
+
+FULL = ["tiny_fp32", "tiny_fp32_dense", "wan13b", "hunyuan", "wan14b_mixed", "long4x"]
+
+
+def _sample_rows(g, heads, B, n_rows=16, seed=0):
+    rng = np.random.default_rng(seed)
+    order = np.argsort(g.sizes, kind="stable")
+    picks = {int(order[0]), int(order[-1]), int(order[len(order) // 2])}
+    while len(picks) < min(n_rows, g.NB):
+        picks.add(int(rng.integers(0, g.NB)))
+    rows = []
+    for n, i in enumerate(sorted(picks)):
+        rows.append((int(rng.integers(0, B)), int((n * 7) % heads), i))
+    return rows
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", FULL)
+def test_full_workload(vsa, name):
+    w = W.WORKLOADS[name]
+    _say(f"[gpu] full workload {name}: generating")
+    inp = W.generate(w)
+    _say(f"[gpu] full workload {name}: GPU plan+attn")
+    q, k, v, idx, o = _run(vsa, w, inp)
+    grp, gci = _index_np(idx)
+    _say(f"[gpu] full workload {name}: oracle plan")
+    rp, ci, info = O.plan(inp["q"], inp["k"], w.grid, w.block, inp["density"], w.window_t)
+    assert np.array_equal(grp, rp), "row_ptr differs"
+    assert np.array_equal(gci, ci), "col_idx differs"
+    g = info["geometry"]
+    rows = _sample_rows(g, w.heads, w.B) if g.NB > 8 else [(0, h, i) for h in range(w.heads) for i in range(g.NB)]
+    _say(f"[gpu] full workload {name}: oracle attention on {len(rows)} query blocks")
+    og = o.float().cpu().numpy()
+    errs = []
+    for (b, h, i) in rows:
+        ref = O.attention_row(inp["q"], inp["k"], inp["v"], g, rp, ci, b, h, i)
+        got = og[b, h, g.tokens[i]]
+        errs.append(np.abs(got - ref))
+    err = np.concatenate([e.ravel() for e in errs])
+    if w.dtype == "bf16":
+        assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN, (err.max(), err.mean())
+    else:
+        assert err.max() <= F32_MAX, err.max()
+    assert np.all(np.isfinite(og))
+    _say(f"[gpu]   ok nnz={len(ci)} max-abs {err.max():.2e} mean-abs {err.mean():.2e}")
