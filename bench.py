@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark of centroid-scored 3D block-sparse attention on one MI355X.
+
+One step = one attention call of the method: vsa_plan (block means,
+centroid scores, per-row top-k, CSR) followed by vsa_attn (block-sparse
+flash attention with the gather from raster order and the layout restore
+fused in), on the Wan2.1-1.3B 480p/81f shape: B=1, 12 heads, d=128, latent
+21x30x52 (32,760 tokens), 4x4x8 blocks, density 0.20, bf16, synthetic
+smooth-field Q/K and N(0,1) V, resident in HBM before timing starts.
+
+Prints one JSON line.  `value` is executed TFLOP/s of the step (valid
+query-key token pairs of the produced index x 4*d, the convention of
+SPADE Table 2), `ms_per_step` is the time per attention call.
+
+    python bench.py [--steps K] [--warmup W] [--workload wan13b]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms/attn call + executed TFLOP/s (% bf16 MFMA peak), Wan-1.3B shape, density 0.2"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector peak
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_wan13b_traffic.txt")
+
+
+def block_sizes(grid, block):
+    """Tokens per block in block-id order (edge blocks cut short)."""
+    ext = []
+    for n, b in zip(grid, block):
+        e = [b] * (n // b) + ([n % b] if n % b else [])
+        ext.append(np.array(e, dtype=np.int64))
+    return (ext[0][:, None, None] * ext[1][None, :, None] * ext[2][None, None, :]).reshape(-1)
+
+
+def executed_flops(row_ptr, col_idx, sizes, D):
+    """4*D per valid (query token, kept key token) pair."""
+    NB = len(sizes)
+    lens = np.diff(row_ptr)
+    rows = np.arange(len(lens)) % NB
+    per_entry_q = np.repeat(sizes[rows], lens)
+    return int(4 * D * np.sum(per_entry_q * sizes[col_idx[: row_ptr[-1]]]))
+
+
+def padded_flops(row_ptr, col_idx, sizes, D, q_tile=32, k_tile=32):
+    """Work the attention kernel issues: query rows rounded up to 32 per wave,
+    keys rounded up to 32 per stage half."""
+    NB = len(sizes)
+    lens = np.diff(row_ptr)
+    rows = np.arange(len(lens)) % NB
+    qp = -(-sizes // q_tile) * q_tile
+    kp = -(-sizes // k_tile) * k_tile
+    return int(4 * D * np.sum(np.repeat(qp[rows], lens) * kp[col_idx[: row_ptr[-1]]]))
+
+
+def read_traffic(src_hash):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current attention kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            a, b = line.split(":", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("kernel_source_sha256") != src_hash:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def kernel_source_hash():
+    import hashlib
+    p = os.path.join(ROOT, "block_sparse_attention_centroids_amd", "csrc", "attn.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()
+
+
+def cpu_baseline(inp, w, row_ptr, col_idx, sizes, step_flops, budget_s=20.0):
+    """The CPU oracle timed on the host: its full plan, plus its float64
+    attention on a seeded sample of query blocks, scaled to a whole step."""
+    from oracle import vsa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    t0 = time.perf_counter()
+    rp, ci, info = O.plan(inp["q"], inp["k"], w.grid, w.block, inp["density"], w.window_t)
+    t_plan = time.perf_counter() - t0
+    g = info["geometry"]
+    rng = np.random.default_rng(0)
+    t_attn, f_attn, n_rows = 0.0, 0, 0
+    while t_attn < budget_s and n_rows < 4 * g.NB:
+        b, h, i = int(rng.integers(0, w.B)), int(rng.integers(0, w.heads)), int(rng.integers(0, g.NB))
+        r = (b * w.heads + h) * g.NB + i
+        t0 = time.perf_counter()
+        O.attention_row(inp["q"], inp["k"], inp["v"], g, rp, ci, b, h, i)
+        t_attn += time.perf_counter() - t0
+        f_attn += 4 * w.D * int(sizes[i]) * int(sizes[ci[rp[r]: rp[r + 1]]].sum())
+        n_rows += 1
+    t_step = t_plan + t_attn * (step_flops / max(f_attn, 1))
+    return {"value": step_flops / t_step / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": (f"full oracle plan ({t_plan:.2f} s) + float64 oracle attention on {n_rows} "
+                       f"seeded query blocks ({t_attn:.1f} s, {f_attn / 1e9:.1f} GFLOP), scaled to "
+                       f"the step's {step_flops / 1e12:.3f} TFLOP"),
+            "seconds_per_step": t_step}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan13b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              "(the method would shard by head with no exchange between GPUs)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    import block_sparse_attention_centroids_amd as vsa
+
+    vsa.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    w = W.WORKLOADS[a.workload]
+    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+    inp = W.generate(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda", 0)
+    q, k, v = (torch.from_numpy(inp[n]).to(dev, dt).contiguous() for n in ("q", "k", "v"))
+    dens = [float(d) for d in inp["density"]]
+    torch.cuda.synchronize()
+
+    def step():
+        idx = vsa.plan(q, k, w.grid, w.block, dens, w.window_t)
+        return idx, vsa.attn(q, k, v, idx)
+
+    print(f"[bench] warmup {a.warmup}", file=sys.stderr, flush=True)
+    for _ in range(a.warmup):
+        idx, o = step()
+    torch.cuda.synchronize()
+
+    # Pre-allocate the plan's buffers so the timed loop does not allocate:
+    # the same index is re-planned in place every step.
+    import ctypes
+    from block_sparse_attention_centroids_amd import _lib
+    lib = _lib.load()
+    shape = idx.shape
+    rl, cap, pws, _ = vsa.query(shape, dens, w.window_t)
+    ws = torch.empty(max(pws, 1), dtype=torch.uint8, device=dev)
+    darr = (ctypes.c_float * len(dens))(*dens)
+    cidx = idx.c_index()
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    qp, kp, vp, op = (ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, o))
+
+    def plan_call():
+        _lib.check(lib.vsa_plan(qp, kp, ctypes.byref(shape), darr, len(dens), w.window_t,
+                                ctypes.byref(cidx), ctypes.c_void_p(ws.data_ptr()), ws.numel(), sp), "vsa_plan")
+
+    def attn_call():
+        _lib.check(lib.vsa_attn(qp, kp, vp, ctypes.byref(cidx), ctypes.c_float(0.0), op, None, 0, sp), "vsa_attn")
+
+    for _ in range(2):
+        plan_call(); attn_call()
+    torch.cuda.synchronize()
+
+    K = a.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        ev[s][0].record(stream)
+        plan_call()
+        ev[s][1].record(stream)
+        attn_call()
+        ev[s][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    plan_ms = np.array([ev[s][0].elapsed_time(ev[s][1]) for s in range(K)])
+    attn_ms = np.array([ev[s][1].elapsed_time(ev[s][2]) for s in range(K)])
+    step_ms = np.array([ev[s][0].elapsed_time(ev[s][2]) for s in range(K)])
+    ms_per_step = wall * 1e3 / K
+
+    rp = idx.row_ptr.cpu().numpy().astype(np.int64)
+    ci = idx.col_idx.cpu().numpy().astype(np.int64)
+    sizes = block_sizes(w.grid, w.block)
+    flops = executed_flops(rp, ci, sizes, w.D)
+    pflops = padded_flops(rp, ci, sizes, w.D)
+    attn_tflops = flops / (attn_ms.mean() * 1e-3) / 1e12
+    step_tflops = flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    traffic = read_traffic(kernel_source_hash())
+    result = {
+        "metric": METRIC,
+        "value": round(step_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded smooth-field Q/K, N(0,1) V; no dataset or weights)",
+        "config": {"workload": w.name, "B": w.B, "heads": w.heads, "D": w.D, "grid": list(w.grid),
+                   "block": list(w.block), "density": dens[0] if len(set(dens)) == 1 else dens,
+                   "window_t": w.window_t},
+        "roofline": {"bound": "mfma" if w.dtype == "bf16" else "alu",
+                     "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / peak, 4), "traffic": traffic},
+        "attn_ms": round(float(attn_ms.mean()), 4),
+        "attn_ms_p10_p50_p90": [round(float(x), 4) for x in np.percentile(attn_ms, [10, 50, 90])],
+        "plan_ms": round(float(plan_ms.mean()), 4),
+        "step_ms_events": round(float(step_ms.mean()), 4),
+        "attn_tflops": round(attn_tflops, 2),
+        "pct_bf16_peak_attn": round(100 * attn_tflops / peak, 2),
+        "pct_bf16_peak_step": round(100 * step_tflops / peak, 2),
+        "executed_tflop": round(flops / 1e12, 4),
+        "issued_tflop_32x32_tiles": round(pflops / 1e12, 4),
+        "nnz_blocks": int(rp[-1]),
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    if not a.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(inp, w, rp, ci, sizes, flops, a.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
