@@ -127,6 +127,8 @@ def main():
     ap.add_argument("--workload", default="wan13b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run one plain device-to-device copy of MIB MiB (HBM counter scale)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
@@ -141,6 +143,15 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if a.copy_calibration:
+        n = a.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n}))
+        return
     w = W.WORKLOADS[a.workload]
     print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
     inp = W.generate(w)

@@ -11,11 +11,13 @@
 //   online softmax in float32        the lane owns one query column, so the
 //                                    row max/sum are in-lane plus one swap
 //                                    with the lane 32 away
-//   O^T (d x queries) += V^T P^T     V^T from LDS ([d][key], transposed on
-//                                    the way in), P^T straight from the S^T
-//                                    accumulators (same lane, same keys)
-// K/V stages are loaded into registers one stage ahead, so global latency
-// overlaps the matrix work of the current stage.
+//   O^T (d x queries) += V^T P^T     V^T fragments read from the row-major
+//                                    V tile with the transposing LDS read,
+//                                    P^T straight from the S^T accumulators
+//                                    (same lane, same keys)
+// K/V stages are loaded into registers one stage ahead through raw buffer
+// loads (out-of-range reads return zero), so global latency overlaps the
+// matrix work of the current stage.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -26,38 +28,174 @@
 namespace vsa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-constexpr int KT = 64;        // keys per stage
-constexpr int VT_LD = KT + 4; // V^T row pitch in bf16 (136 B: conflict-free b64 reads)
+constexpr int KS = 32;              // keys per stage
+constexpr int NBUF = 4;             // LDS ring: PV(t), QK(t+1), stage t+2 landing, stage t+3 landing
+#ifndef VSA_ATTN_NT
+#define VSA_ATTN_NT 1
+#endif
+constexpr int NT = VSA_ATTN_NT;     // 32-query MFMA tiles per wave
+constexpr int WAVES = 4 / NT;       // waves per workgroup: 128 query tokens in all
+constexpr int THREADS = 64 * WAVES;
+constexpr int QPW = 32 * NT;        // query tokens per wave
+constexpr float LAZY_LOG2 = 8.0f;   // running max is only raised when a row max exceeds it by 2^8
 
-template <int D>
-struct AttnCfg {
-  static constexpr int KS_LD = D + 8;            // K row pitch in bf16 (16 B pad)
-  static constexpr int PARTS = D / 8;            // 16-byte pieces per token row
-  static constexpr int KPT = KT * PARTS / 256;   // K pieces per thread per stage
-  static constexpr int KROWS = 256 / PARTS;      // K rows covered per pass
-  static constexpr int VGROUPS = (KT / 4) * PARTS;  // (4 keys x 8 d) groups per stage
-};
-
-__device__ inline uint32_t bf16_pair(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
-
-__device__ inline uint16_t u4_elem(const u32x4_t& v, int e) {
-  const uint32_t w = v[e >> 1];
-  return (e & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffffu);
+// LDS tiles hold token rows of D bf16 (PARTS 16-byte pieces) with no
+// padding; piece pc of row r sits at slot pc ^ swz(r) of the row.  The
+// swizzle keeps both fragment reads conflict-free: the K reads (16 lanes,
+// 16 rows, one piece) and the transposing V reads (32 lanes, 4 rows, 4
+// consecutive pieces).
+template <int PARTS>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (PARTS == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
+struct AttnCfg {
+  static constexpr int PARTS = D / 8;                  // 16-byte pieces per token row
+  static constexpr int TILE_BYTES = KS * D * 2;        // one K or V stage tile
+  static constexpr int ROWS_PER_INST = 64 / PARTS;     // rows one wave instruction fills
+  static constexpr int IPW = KS / ROWS_PER_INST / WAVES;  // load instructions per wave per tensor
+};
+
+// Raw buffer descriptor: loads past `bytes` return zero instead of faulting.
+// The base address is made explicitly wave-uniform so the descriptor stays
+// in scalar registers.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Raw buffer descriptor as four scalar dwords (base, num_records, flags).
+struct Rsrc4 {
+  u32x4_t d;
+};
+__device__ inline Rsrc4 make_rsrc4(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  Rsrc4 r;
+  r.d[0] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.d[1] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));   // stride 0
+  r.d[2] = bytes;
+  r.d[3] = 0x00020000u;
+  return r;
+}
+
+// 16 bytes per lane from a raw buffer straight into LDS at lds_base + 16*lane
+// (out-of-range offsets write zeros).  Written as asm so that the
+// compiler's LDS-DMA tracking does not force a wait for every in-flight
+// stage before each LDS read: completion is awaited explicitly (vmcnt)
+// before the barrier that publishes a stage.  The instruction has no
+// register results.
+__device__ __forceinline__ void dma16(const Rsrc4& r, uint32_t lds_base, uint32_t voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_base), "v"(voff), "s"(r.d)
+      : "memory", "m0");
+}
+
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ inline uint32_t bf16_pair(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// The key block a CSR entry names, with everything the loaders need; all
+// fields are wave-uniform.
+struct KeyBlock {
+  int nj;            // tokens in the block
+  bool nominal;      // (h, w) extents are the nominal block's
+  uint32_t jbase;    // byte offset of the block's origin token in the head
+  TokenMap map;      // token index -> raster index (for the other blocks)
+};
+
+template <int D>
+__device__ __forceinline__ KeyBlock open_block(const DGeo& g, const int32_t* __restrict__ col_idx, int entry,
+                                               bool stage_rows) {
+  const int j = uniform(min(max(col_idx[entry], 0), g.NB - 1));   // a corrupt index cannot leave the head
+  const Box bj = block_box(g, j);
+  KeyBlock kb;
+  kb.nj = bj.n();
+  kb.nominal = bj.eh == g.bh && bj.ew == g.bw && stage_rows;
+  kb.map.base = (bj.t0 * g.H + bj.h0) * g.W + bj.w0;
+  kb.jbase = (uint32_t)kb.map.base * (D * 2);
+  if (!kb.nominal) kb.map.init(g, bj);   // the reciprocals are only needed off the fast path
+  return kb;
+}
+
+// Online-softmax step for one 32-key x 32-query tile of S^T held by this
+// lane (query column l32; 16 of the 32 keys): masks keys past `nv`, applies
+// the lazy rescale to the tile's O^T accumulators, and returns P^T as two
+// bf16x8 B-operand fragments.
+template <int D>
+__device__ __forceinline__ void softmax_tile(f32x16_t& s, int nv, int g2, float scale_log2, float tau,
+                                             float& m_run, float& l_run, f32x16_t (&acc)[D / 32],
+                                             bf16x8_t (&pb)[2]) {
+  if (nv < KS) {   // only a block's last, partial stage (kept as a real branch)
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int key = 8 * (rr >> 2) + 4 * g2 + (rr & 3);
+      s[rr] = key < nv ? s[rr] : -INFINITY;
+    }
+  }
+  float mx = fmaxf(s[0], s[1]);
+#pragma unroll
+  for (int rr = 2; rr < 16; rr += 2) mx = fmaxf(mx, fmaxf(s[rr], s[rr + 1]));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  // Lazy rescale: the running max moves only when some row max exceeds it
+  // by more than 2^LAZY_LOG2; otherwise p <= 2^LAZY_LOG2 stays exact enough
+  // in bf16 and the O/l rescale is skipped for the whole wave.
+  if (__ballot(mx > m_run + tau) != 0ull) {
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) acc[c] *= alpha;
+    l_run *= alpha;
+    m_run = m_new;
+  }
+  const float mb = m_run * scale_log2;
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    f32x8_t pf;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) pf[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * m + t], scale_log2, -mb));
+    pb[m] = __builtin_convertvector(pf, bf16x8_t);
+#pragma unroll
+    for (int t = 0; t < 8; t += 2) {
+      const bf16x2_t pr = {pb[m][t], pb[m][t + 1]};
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2 / NT, 2 / NT))) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     DGeo g, float scale_log2) {
   using C = AttnCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * C::KS_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VT_LD];
+  constexpr int PARTS = C::PARTS;
+  // [buffer][K tile, V tile]
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * 2 * C::TILE_BYTES];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, g2 = lane >> 5;
@@ -76,186 +214,234 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   TokenMap qmap;
   qmap.init(g, bi);
   const size_t head_off = (size_t)bh * g.N * D;
-  const uint16_t* kh = k + head_off;
-  const uint16_t* vh = v + head_off;
+  const uint32_t head_bytes = (uint32_t)g.N * D * 2u;
+  const Rsrc4 krs = make_rsrc4(k + head_off, head_bytes);
+  const Rsrc4 vrs = make_rsrc4(v + head_off, head_bytes);
+  const uint32_t lds0 = (uint32_t)uniform((int)lds_addr(lds));
 
-  // Q^T fragments (B operand): query column l32, channels 16*ks + 8*g2 + [0, 8).
-  const int qtok = wave * 32 + l32;
-  const bool wave_active = wave * 32 < ni;
-  bf16x8_t qf[D / 16];
-  {
+  // This wave's query tiles: tokens [QPW*wave + 32*t, +32) of the block.
+  const int ntiles = min(NT, max(0, (ni - QPW * wave + 31) / 32));   // wave-uniform
+  // Q^T fragments (B operand): query column l32 of tile t, channels 16*ks + 8*g2 + [0, 8).
+  bf16x8_t qf[NT][D / 16];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int qtok = QPW * wave + 32 * t + l32;
     const bool ok = qtok < ni;
     const uint16_t* qp = q + head_off + (size_t)(ok ? qmap(qtok) : 0) * D + g2 * 8;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       u32x4_t raw = ok ? *reinterpret_cast<const u32x4_t*>(qp + ks * 16) : u32x4_t{0u, 0u, 0u, 0u};
-      qf[ks] = __builtin_bit_cast(bf16x8_t, raw);
+      qf[t][ks] = __builtin_bit_cast(bf16x8_t, raw);
     }
   }
 
-  f32x16_t acc[D / 32];
+  f32x16_t acc[NT][D / 32];
 #pragma unroll
-  for (int c = 0; c < D / 32; ++c) acc[c] = f32x16_t{};
-  float m_run = -INFINITY, l_run = 0.0f;
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) acc[t][c] = f32x16_t{};
+  float m_run[NT], l_run[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) { m_run[t] = -INFINITY; l_run[t] = 0.0f; }
+  const float tau = LAZY_LOG2 / scale_log2;
 
   const int row = bh * g.NB + i;
-  const int e0 = row_ptr[row], e1 = row_ptr[row + 1];
+  const int e_end = uniform(row_ptr[row + 1]);
+  int e_ld = uniform(row_ptr[row]);
 
-  // Loader roles.  K: piece p of this thread covers key (tid / PARTS) +
-  // KROWS * p, bytes [16 * (tid % PARTS), +16).  V: keys 4*kg .. 4*kg+3 at
-  // channels 8*dpart .. 8*dpart+7, written transposed.
-  const int kpart = tid % C::PARTS, krow0 = tid / C::PARTS;
-  const int vkg = tid & 15, vdpart = tid >> 4;
-  const bool vloader = tid < C::VGROUPS;
-  u32x4_t kreg[C::KPT], vreg[4];
-
-  int e = e0, c0 = 0;
-  int j = 0, nj = 0, nvalid = 0;
-  TokenMap kmap;
-  auto fetch = [&](int jj, int cstart, int nv) {
+  // Loader role.  Load instruction n of this wave fills slots
+  // [64*(wave*IPW + n), +64) of a tile: lane L writes row
+  // r_n = (wave*IPW + n)*ROWS_PER_INST + L/PARTS, slot L%PARTS, which holds
+  // piece (L%PARTS) ^ swz(r_n) of that key's token row.  When a stage spans
+  // whole rows of the nominal box (KS a multiple of bw, and KS and bh*bw
+  // multiples of one another) the source offset inside a nominal block is
+  // the offset in the first stage plus a wave-uniform step per stage.
+  const int nom_hw = g.bh * g.bw;
+  const bool stage_rows = (KS % g.bw == 0) && (KS % nom_hw == 0 || nom_hw % KS == 0);
+  int ld_row[C::IPW];
+  uint32_t ld_piece[C::IPW], ld_rel[C::IPW];
 #pragma unroll
-    for (int p = 0; p < C::KPT; ++p) {
-      const int key = krow0 + C::KROWS * p;
-      kreg[p] = key < nv ? *reinterpret_cast<const u32x4_t*>(kh + (size_t)kmap(cstart + key) * D + kpart * 8)
-                         : u32x4_t{0u, 0u, 0u, 0u};
-    }
-    if (vloader) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = vkg * 4 + r;
-        vreg[r] = key < nv ? *reinterpret_cast<const u32x4_t*>(vh + (size_t)kmap(cstart + key) * D + vdpart * 8)
-                           : u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
-    (void)jj;
-  };
-
-  // A corrupt index must not send loads out of bounds: block ids are clamped.
-  if (e < e1) {
-    j = min(max(col_idx[e], 0), g.NB - 1);
-    const Box bj = block_box(g, j);
-    nj = bj.n();
-    kmap.init(g, bj);
-    nvalid = min(KT, nj);
-    fetch(j, 0, nvalid);
+  for (int n = 0; n < C::IPW; ++n) {
+    const int r = (wave * C::IPW + n) * C::ROWS_PER_INST + lane / PARTS;
+    ld_row[n] = r;
+    ld_piece[n] = (uint32_t)(((lane % PARTS) ^ swz<PARTS>(r)) * 16);
+    const int ut = r / nom_hw, rr = r - ut * nom_hw;
+    const int uh = rr / g.bw, uw = rr - uh * g.bw;
+    ld_rel[n] = (uint32_t)((ut * g.H * g.W + uh * g.W + uw) * D * 2) + ld_piece[n];
   }
 
-  while (e < e1) {
-    const int nv_cur = nvalid;
-    __syncthreads();   // every wave is done with the previous stage
-#pragma unroll
-    for (int p = 0; p < C::KPT; ++p)
-      *reinterpret_cast<u32x4_t*>(&Ks[(krow0 + C::KROWS * p) * C::KS_LD + kpart * 8]) = kreg[p];
-    if (vloader) {
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        u32x2_t w;
-        w[0] = bf16_pair(u4_elem(vreg[0], dd), u4_elem(vreg[1], dd));
-        w[1] = bf16_pair(u4_elem(vreg[2], dd), u4_elem(vreg[3], dd));
-        *reinterpret_cast<u32x2_t*>(&Vt[(vdpart * 8 + dd) * VT_LD + vkg * 4]) = w;
-      }
-    }
-    __syncthreads();
+  // Loader cursor: the next stage to fetch is (entry e_ld, tokens from c_ld).
+  int c_ld = 0;
+  KeyBlock blk;
+  blk.nj = 0;
+  if (e_ld < e_end) blk = open_block<D>(g, col_idx, e_ld, stage_rows);
 
-    // Advance and prefetch the next stage.
-    int e_next = e, c_next = c0 + KT;
-    if (c_next >= nj) { e_next = e + 1; c_next = 0; }
-    if (e_next < e1) {
-      if (e_next != e) {
-        j = min(max(col_idx[e_next], 0), g.NB - 1);
-        const Box bj = block_box(g, j);
-        nj = bj.n();
-        kmap.init(g, bj);
-      }
-      nvalid = min(KT, nj - c_next);
-      fetch(j, c_next, nvalid);
-    }
+  // Issue the stage at the cursor as direct-to-LDS loads into buffer BUF and
+  // advance; NV receives its valid key count (0 when the row is exhausted).
+  // Rows past the block's end read out of range and land as zeros.
+#define VSA_LOAD_STAGE(BUF, NV)                                                               \
+  do {                                                                                        \
+    if (e_ld < e_end) {                                                                       \
+      const int nv_ = min(KS, blk.nj - c_ld);                                                 \
+      const bool fast_ = blk.nominal;                                                         \
+      const int sut_ = c_ld / nom_hw, suh_ = (c_ld - sut_ * nom_hw) / g.bw;                   \
+      const uint32_t step_ = blk.jbase + (uint32_t)((sut_ * g.H + suh_) * g.W) * (D * 2);     \
+      const uint32_t kt_ = (uint32_t)uniform((int)(lds0 + (BUF) * 2 * C::TILE_BYTES + wave * C::IPW * 1024)); \
+      _Pragma("unroll") for (int n = 0; n < C::IPW; ++n) {                                     \
+        uint32_t off = fast_ ? step_ + ld_rel[n]                                              \
+                             : (uint32_t)blk.map(c_ld + ld_row[n]) * (D * 2) + ld_piece[n];   \
+        off = ld_row[n] < nv_ ? off : 0x80000000u;                                            \
+        dma16(krs, kt_ + n * 1024, off);                                                      \
+        dma16(vrs, kt_ + C::TILE_BYTES + n * 1024, off);                                      \
+      }                                                                                       \
+      (NV) = nv_;                                                                             \
+      c_ld += KS;                                                                             \
+      if (c_ld >= blk.nj) {                                                                   \
+        c_ld = 0;                                                                             \
+        ++e_ld;                                                                               \
+        if (e_ld < e_end) blk = open_block<D>(g, col_idx, e_ld, stage_rows);                              \
+      }                                                                                       \
+    } else {                                                                                  \
+      (NV) = 0;                                                                               \
+    }                                                                                         \
+  } while (0)
 
-    if (wave_active) {
-      const int halves = nv_cur > 32 ? 2 : 1;
-      f32x16_t s[2];
-      s[0] = f32x16_t{};
-      s[1] = f32x16_t{};
+  // Per-lane fragment byte offsets within a stage's tiles.
+  // K (A operand of S^T = K Q^T): row l32, piece 2*ks + g2.
+  uint32_t kaddr[D / 16];
+  {
+    const int sw = swz<PARTS>(l32);
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        if (hf < halves) {
-#pragma unroll
-          for (int ks = 0; ks < D / 16; ++ks) {
-            const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(&Ks[(hf * 32 + l32) * C::KS_LD + ks * 16 + g2 * 8]);
-            s[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, raw), qf[ks], s[hf], 0, 0, 0);
-          }
-        }
-      }
-      // Mask keys past the block's end; in-lane max over this lane's keys.
-      float mx = -INFINITY;
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int key = hf * 32 + 8 * (rr >> 2) + 4 * g2 + (rr & 3);
-          const float x = key < nv_cur ? s[hf][rr] : -INFINITY;
-          s[hf][rr] = x;
-          mx = fmaxf(mx, x);
-        }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
-      m_run = m_new;
-      const float mb = m_new * scale_log2;
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c) acc[c] *= alpha;
-      l_run *= alpha;
-      bf16x8_t pb[2][2];
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          f32x8_t pf;
-#pragma unroll
-          for (int t = 0; t < 8; ++t) pf[t] = __builtin_amdgcn_exp2f(s[hf][8 * m + t] * scale_log2 - mb);
-          pb[hf][m] = __builtin_convertvector(pf, bf16x8_t);
-#pragma unroll
-          for (int t = 0; t < 8; ++t) l_run += (float)pb[hf][m][t];
-        }
-      }
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        if (hf < halves) {
-#pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            const int kb = hf * 32 + 16 * m + 4 * g2;
-#pragma unroll
-            for (int c = 0; c < D / 32; ++c) {
-              const uint16_t* vp = &Vt[(c * 32 + l32) * VT_LD + kb];
-              u32x4_t raw;
-              const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vp);
-              const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vp + 8);
-              raw[0] = lo[0]; raw[1] = lo[1]; raw[2] = hi[0]; raw[3] = hi[1];
-              acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, raw), pb[hf][m], acc[c], 0, 0, 0);
-            }
-          }
-        }
-      }
-    }
-    e = e_next;
-    c0 = c_next;
+    for (int ks = 0; ks < D / 16; ++ks) kaddr[ks] = (uint32_t)((l32 * PARTS + ((2 * ks + g2) ^ sw)) * 16);
   }
+  // V^T (A operand of O^T = V^T P^T) through the transposing read: lane
+  // (r16, dhalf, g2) addresses row 16*m + 8*hi + 4*g2 + r16/4 and the 8 bytes
+  // at byte 64*c + 32*dhalf + 8*(r16 & 3) of it.
+  uint32_t vaddr[2][D / 32];
+  {
+    const int r16 = lane & 15, dhalf = (lane >> 4) & 1;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int r = 8 * hi + 4 * g2 + (r16 >> 2);
+      const int sw = swz<PARTS>(r);
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) {
+        const int byte = 64 * c + 32 * dhalf + 8 * (r16 & 3);
+        vaddr[hi][c] = (uint32_t)(r * PARTS * 16 + (((byte >> 4) ^ sw) << 4) + (byte & 15));
+      }
+    }
+  }
+
+  // Prologue: stages 0..2 issued into buffers 0..2; stages 0 and 1 waited for.
+  int nv0 = 0, nv1 = 0, nv2 = 0;
+  VSA_LOAD_STAGE(0, nv0);
+  VSA_LOAD_STAGE(1, nv1);
+  VSA_LOAD_STAGE(2, nv2);
+  __builtin_amdgcn_s_waitcnt(0);   // all of this wave's loads
+  __syncthreads();
+
+  f32x16_t s_cur[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) s_cur[t] = f32x16_t{};
+  if (ntiles > 0 && nv0 > 0) {
+    const uint8_t* kt = lds;
+    u32x4_t kfr[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) kfr[ks] = *reinterpret_cast<const u32x4_t*>(kt + kaddr[ks]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      if (t < ntiles)
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+          s_cur[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kfr[ks]), qf[t][ks], s_cur[t], 0, 0, 0);
+  }
+
+  // Iteration t: softmax and PV of stage t (buffer t%4), QK of stage t+1,
+  // stage t+3 issued into buffer (t+3)%4 (last read by PV(t-1), which every
+  // wave finished before this iteration's barrier).  The loop is unrolled
+  // over the ring so buffer offsets are constants and the two S^T register
+  // sets swap roles instead of being copied.
+#define VSA_ITER(BC, S_CUR, S_NXT)                                                            \
+  {                                                                                           \
+    /* Stage t+1 was issued two iterations ago: all but one stage of this */                  \
+    /* wave's loads are complete; the barrier makes every wave's visible. */                  \
+    if (nv2 > 0) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * C::IPW));                           \
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                                                  \
+    __syncthreads();                                                                          \
+    int nv3 = 0;                                                                              \
+    VSA_LOAD_STAGE(((BC) + 3) & 3, nv3);                                                      \
+    if (ntiles > 0) {                                                                         \
+      const uint8_t* kt = lds + (((BC) + 1) & 3) * 2 * C::TILE_BYTES;                         \
+      if (nv1 > 0) {                                                                          \
+        u32x4_t kfr[D / 16];                                                                  \
+        _Pragma("unroll") for (int ks = 0; ks < D / 16; ++ks)                                  \
+          kfr[ks] = *reinterpret_cast<const u32x4_t*>(kt + kaddr[ks]);                        \
+        _Pragma("unroll") for (int t = 0; t < NT; ++t)                                         \
+          if (t < ntiles) {                                                                   \
+            S_NXT[t] = f32x16_t{};                                                            \
+            _Pragma("unroll") for (int ks = 0; ks < D / 16; ++ks)                              \
+              S_NXT[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                             \
+                  __builtin_bit_cast(bf16x8_t, kfr[ks]), qf[t][ks], S_NXT[t], 0, 0, 0);       \
+          }                                                                                   \
+      }                                                                                       \
+      __builtin_amdgcn_sched_barrier(0);                                                      \
+      const uint8_t* vt = lds + (BC) * 2 * C::TILE_BYTES + C::TILE_BYTES;                     \
+      i16x4_t vfr[2][2][D / 32];                                                              \
+      _Pragma("unroll") for (int m = 0; m < 2; ++m)                                            \
+        _Pragma("unroll") for (int hi = 0; hi < 2; ++hi)                                       \
+          _Pragma("unroll") for (int c = 0; c < D / 32; ++c)                                   \
+            vfr[m][hi][c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(                          \
+                (lds_i16x4_t*)(vt + vaddr[hi][c] + m * 16 * PARTS * 16));                     \
+      _Pragma("unroll") for (int t = 0; t < NT; ++t) {                                         \
+        if (t < ntiles) {                                                                     \
+          bf16x8_t pb[2];                                                                     \
+          softmax_tile<D>(S_CUR[t], nv0, g2, scale_log2, tau, m_run[t], l_run[t], acc[t], pb); \
+          _Pragma("unroll") for (int m = 0; m < 2; ++m)                                        \
+            _Pragma("unroll") for (int c = 0; c < D / 32; ++c) {                               \
+              const i16x8_t both = __builtin_shufflevector(vfr[m][0][c], vfr[m][1][c], 0, 1, 2, 3, 4, 5, 6, 7); \
+              acc[t][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                            \
+                  __builtin_bit_cast(bf16x8_t, both), pb[m], acc[t][c], 0, 0, 0);             \
+            }                                                                                 \
+        }                                                                                     \
+      }                                                                                       \
+    }                                                                                         \
+    nv0 = nv1; nv1 = nv2; nv2 = nv3;                                                          \
+  }
+
+  f32x16_t s_b[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) s_b[t] = f32x16_t{};
+  while (true) {
+    if (nv0 == 0) break;
+    VSA_ITER(0, s_cur, s_b);
+    if (nv0 == 0) break;
+    VSA_ITER(1, s_b, s_cur);
+    if (nv0 == 0) break;
+    VSA_ITER(2, s_cur, s_b);
+    if (nv0 == 0) break;
+    VSA_ITER(3, s_b, s_cur);
+  }
+#undef VSA_ITER
+#undef VSA_LOAD_STAGE
 
   // Epilogue: O = O^T / l, rounded to bf16, stored at the query's raster row.
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (qtok < ni) {
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    uint16_t* op = o + head_off + (size_t)qmap(qtok) * D;
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
+  for (int t = 0; t < NT; ++t) {
+    const float l_tot = l_run[t] + __shfl_xor(l_run[t], 32, 64);
+    const int qtok = QPW * wave + 32 * t + l32;
+    if (qtok < ni) {
+      const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+      uint16_t* op = o + head_off + (size_t)qmap(qtok) * D;
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d = c * 32 + 8 * gq + 4 * g2;
-        u32x2_t w;
-        w[0] = bf16_pair(f32_to_bf16(acc[c][4 * gq + 0] * inv), f32_to_bf16(acc[c][4 * gq + 1] * inv));
-        w[1] = bf16_pair(f32_to_bf16(acc[c][4 * gq + 2] * inv), f32_to_bf16(acc[c][4 * gq + 3] * inv));
-        *reinterpret_cast<u32x2_t*>(op + d) = w;
+      for (int c = 0; c < D / 32; ++c) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int d = c * 32 + 8 * gq + 4 * g2;
+          u32x2_t w;
+          w[0] = bf16_pair(f32_to_bf16(acc[t][c][4 * gq + 0] * inv), f32_to_bf16(acc[t][c][4 * gq + 1] * inv));
+          w[1] = bf16_pair(f32_to_bf16(acc[t][c][4 * gq + 2] * inv), f32_to_bf16(acc[t][c][4 * gq + 3] * inv));
+          *reinterpret_cast<u32x2_t*>(op + d) = w;
+        }
       }
     }
   }
@@ -336,10 +522,10 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, void* o, int
   if (dtype == VSA_BF16) {
     const float sl2 = scale * 1.4426950408889634f;
     if (D == 128)
-      hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(nwg), dim3(256), 0, st, (const uint16_t*)q,
+      hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(nwg), dim3(THREADS), 0, st, (const uint16_t*)q,
                          (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, row_ptr, col_idx, g, sl2);
     else
-      hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(nwg), dim3(256), 0, st, (const uint16_t*)q,
+      hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(nwg), dim3(THREADS), 0, st, (const uint16_t*)q,
                          (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, row_ptr, col_idx, g, sl2);
   } else {
     if (D == 128)

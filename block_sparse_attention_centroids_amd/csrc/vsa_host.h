@@ -79,6 +79,8 @@ inline vsa_status check_shape(const vsa_shape* s) {
   (void)box;
   int64_t N = int64_t(s->T) * s->H * s->W;
   if (N > (int64_t(1) << 30)) return VSA_ERR_UNSUPPORTED;
+  // One head's tensor must be addressable with 32-bit byte offsets.
+  if (N * s->D * elt_bytes(s->dtype) >= (int64_t(1) << 31)) return VSA_ERR_UNSUPPORTED;
   int64_t elems = int64_t(s->B) * s->heads * N * s->D;
   if (elems > (int64_t(1) << 40)) return VSA_ERR_UNSUPPORTED;
   Geo g = make_geo(*s);
