@@ -15,12 +15,20 @@ using namespace vsa;
 
 namespace {
 
+// ceil(2^32 / d) for 2 <= d < 2^16; 0 stands for d = 1.
+uint32_t div_magic_for(uint32_t d) {
+  if (d <= 1) return 0u;
+  return (uint32_t)(((uint64_t(1) << 32) + d - 1) / d);
+}
+
 DGeo to_dgeo(const Geo& g) {
   DGeo d;
   d.T = g.T; d.H = g.H; d.W = g.W;
   d.bt = g.bt; d.bh = g.bh; d.bw = g.bw;
   d.nbt = g.nbt; d.nbh = g.nbh; d.nbw = g.nbw;
   d.NB = g.NB; d.N = g.N;
+  d.magic_hw = div_magic_for(uint32_t(g.nbh * g.nbw));
+  d.magic_w = div_magic_for(uint32_t(g.nbw));
   return d;
 }
 

@@ -130,11 +130,11 @@ template <int D>
 __device__ __forceinline__ KeyBlock open_block(const DGeo& g, const int32_t* __restrict__ col_idx, int entry,
                                                bool stage_rows) {
   const int j = uniform(min(max(col_idx[entry], 0), g.NB - 1));   // a corrupt index cannot leave the head
-  const Box bj = block_box(g, j);
+  const Box bj = block_box_fast(g, j);
   KeyBlock kb;
-  kb.nj = bj.n();
-  kb.nominal = bj.eh == g.bh && bj.ew == g.bw && stage_rows;
-  kb.map.base = (bj.t0 * g.H + bj.h0) * g.W + bj.w0;
+  kb.nj = uniform(bj.n());
+  kb.nominal = uniform(bj.eh == g.bh && bj.ew == g.bw && stage_rows) != 0;
+  kb.map.base = uniform((bj.t0 * g.H + bj.h0) * g.W + bj.w0);
   kb.jbase = (uint32_t)kb.map.base * (D * 2);
   if (!kb.nominal) kb.map.init(g, bj);   // the reciprocals are only needed off the fast path
   return kb;
@@ -197,7 +197,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2 / NT,
   // [buffer][K tile, V tile]
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * 2 * C::TILE_BYTES];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);   // wave-uniform, so per-wave branches stay scalar
   const int l32 = lane & 31, g2 = lane >> 5;
 
   // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
@@ -258,6 +259,13 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2 / NT,
   // the offset in the first stage plus a wave-uniform step per stage.
   const int nom_hw = g.bh * g.bw;
   const bool stage_rows = (KS % g.bw == 0) && (KS % nom_hw == 0 || nom_hw % KS == 0);
+  // Offset of each 32-key stage slot of a nominal block from its origin.
+  uint32_t slot_off[4];
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl) {
+    const int u = sl * KS, ut = u / nom_hw, uh = (u - ut * nom_hw) / g.bw;
+    slot_off[sl] = (uint32_t)uniform((ut * g.H + uh) * g.W * D * 2);
+  }
   int ld_row[C::IPW];
   uint32_t ld_piece[C::IPW], ld_rel[C::IPW];
 #pragma unroll
@@ -282,10 +290,11 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2 / NT,
 #define VSA_LOAD_STAGE(BUF, NV)                                                               \
   do {                                                                                        \
     if (e_ld < e_end) {                                                                       \
-      const int nv_ = min(KS, blk.nj - c_ld);                                                 \
+      const int nv_ = uniform(min(KS, blk.nj - c_ld));                                        \
       const bool fast_ = blk.nominal;                                                         \
-      const int sut_ = c_ld / nom_hw, suh_ = (c_ld - sut_ * nom_hw) / g.bw;                   \
-      const uint32_t step_ = blk.jbase + (uint32_t)((sut_ * g.H + suh_) * g.W) * (D * 2);     \
+      const int sl_ = c_ld >> 5;                                                              \
+      const uint32_t step_ = blk.jbase + (sl_ == 0 ? slot_off[0] : sl_ == 1 ? slot_off[1]     \
+                                           : sl_ == 2 ? slot_off[2] : slot_off[3]);           \
       const uint32_t kt_ = (uint32_t)uniform((int)(lds0 + (BUF) * 2 * C::TILE_BYTES + wave * C::IPW * 1024)); \
       _Pragma("unroll") for (int n = 0; n < C::IPW; ++n) {                                     \
         uint32_t off = fast_ ? step_ + ld_rel[n]                                              \
@@ -295,11 +304,11 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2 / NT,
         dma16(vrs, kt_ + C::TILE_BYTES + n * 1024, off);                                      \
       }                                                                                       \
       (NV) = nv_;                                                                             \
-      c_ld += KS;                                                                             \
+      c_ld = uniform(c_ld + KS);                                                              \
       if (c_ld >= blk.nj) {                                                                   \
         c_ld = 0;                                                                             \
-        ++e_ld;                                                                               \
-        if (e_ld < e_end) blk = open_block<D>(g, col_idx, e_ld, stage_rows);                              \
+        e_ld = uniform(e_ld + 1);                                                             \
+        if (e_ld < e_end) blk = open_block<D>(g, col_idx, e_ld, stage_rows);                  \
       }                                                                                       \
     } else {                                                                                  \
       (NV) = 0;                                                                               \
@@ -376,6 +385,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2 / NT,
         u32x4_t kfr[D / 16];                                                                  \
         _Pragma("unroll") for (int ks = 0; ks < D / 16; ++ks)                                  \
           kfr[ks] = *reinterpret_cast<const u32x4_t*>(kt + kaddr[ks]);                        \
+        __builtin_amdgcn_sched_barrier(0);                                                    \
         _Pragma("unroll") for (int t = 0; t < NT; ++t)                                         \
           if (t < ntiles) {                                                                   \
             S_NXT[t] = f32x16_t{};                                                            \

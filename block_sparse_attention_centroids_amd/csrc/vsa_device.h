@@ -14,7 +14,20 @@ struct DGeo {
   int nbt, nbh, nbw;
   int NB;
   int N;
+  // ceil(2^32 / d) for d = nbh*nbw and d = nbw (0 encodes d = 1, whose
+  // magic would not fit): for n, d < 2^16, umulhi(n, m) == n / d exactly
+  // (n*d < 2^32 bounds the error below 1).
+  uint32_t magic_hw, magic_w;
 };
+
+// n / d with a precomputed magic (see DGeo); n and d below 2^16.
+__device__ inline int div_magic(int n, uint32_t magic) {
+  return magic == 0u ? n : (int)__umulhi((uint32_t)n, magic);
+}
+
+// Box of block j using the magic divisions (block ids are below 2^16).
+struct Box;
+__device__ inline Box block_box_fast(const DGeo& g, int j);
 
 // The 3D box of block j: origin (t0, h0, w0) and extents (et, eh, ew); edge
 // blocks of a dimension that the box does not divide are cut short.
@@ -28,6 +41,17 @@ __device__ inline Box block_box(const DGeo& g, int j) {
   int per_t = g.nbh * g.nbw;
   int tb = j / per_t, r = j - tb * per_t;
   int hb = r / g.nbw, wb = r - hb * g.nbw;
+  Box b;
+  b.t0 = tb * g.bt; b.h0 = hb * g.bh; b.w0 = wb * g.bw;
+  b.et = min(g.bt, g.T - b.t0);
+  b.eh = min(g.bh, g.H - b.h0);
+  b.ew = min(g.bw, g.W - b.w0);
+  return b;
+}
+
+__device__ inline Box block_box_fast(const DGeo& g, int j) {
+  const int tb = div_magic(j, g.magic_hw), r = j - tb * (g.nbh * g.nbw);
+  const int hb = div_magic(r, g.magic_w), wb = r - hb * g.nbw;
   Box b;
   b.t0 = tb * g.bt; b.h0 = hb * g.bh; b.w0 = wb * g.bw;
   b.et = min(g.bt, g.T - b.t0);

@@ -171,3 +171,12 @@ def test_token_map_division_is_exact():
     inv = (np.float32(1.0) / e).astype(np.float32)
     q = np.floor(((u + np.float32(0.5)).astype(np.float32) * inv).astype(np.float32))
     assert np.array_equal(q.astype(np.int64), (np.arange(128)[:, None] // np.arange(1, 129)[None, :]))
+
+
+def test_magic_division_exact():
+    """Block ids are split with umulhi(n, ceil(2^32/d)) (d = 1 special-cased):
+    exact for every n, d below 2^16 that the geometry can produce."""
+    n = np.arange(1 << 14, dtype=np.uint64)
+    for d in list(range(2, 300)) + [1176, 4096, 16383]:
+        m = np.uint64(((1 << 32) + d - 1) // d)
+        assert np.array_equal((n * m) >> np.uint64(32), n // np.uint64(d)), d
