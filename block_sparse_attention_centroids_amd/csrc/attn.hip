@@ -38,7 +38,7 @@ typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int KS = 32;              // keys per stage
-constexpr int NBUF = 4;             // LDS ring: PV(t), QK(t+1), stage t+2 landing, stage t+3 landing
+constexpr int NBUF = 3;             // LDS ring: stage t (QK and PV), stages t+1 and t+2 landing
 #ifndef VSA_ATTN_NT
 #define VSA_ATTN_NT 1
 #endif
@@ -140,15 +140,22 @@ __device__ __forceinline__ KeyBlock open_block(const DGeo& g, const int32_t* __r
   return kb;
 }
 
-// Online-softmax step for one 32-key x 32-query tile of S^T held by this
-// lane (query column l32; 16 of the 32 keys): masks keys past `nv`, applies
-// the lazy rescale to the tile's O^T accumulators, and returns P^T as two
-// bf16x8 B-operand fragments.
+// Value of the same lane in the other half of the wave (lane ^ 32).
+__device__ __forceinline__ float other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  // r[0]: lanes 32..63 now hold lanes 0..31; r[1]: lanes 0..31 hold lanes 32..63.
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// First half of the online-softmax step for one 32-key x 32-query tile of
+// S^T held by this lane (query column l32; 16 of the 32 keys): masks keys
+// past `nv` (a block's last, partial stage only), takes the row max and
+// applies the lazy rescale to the tile's O^T accumulators.  Returns the
+// exponent offset m*scale*log2(e).
 template <int D>
-__device__ __forceinline__ void softmax_tile(f32x16_t& s, int nv, int g2, float scale_log2, float tau,
-                                             float& m_run, float& l_run, f32x16_t (&acc)[D / 32],
-                                             bf16x8_t (&pb)[2]) {
-  if (nv < KS) {   // only a block's last, partial stage (kept as a real branch)
+__device__ __forceinline__ float softmax_prep(f32x16_t& s, int nv, int g2, float scale_log2, float tau,
+                                              float& m_run, float& l_run, f32x16_t (&acc)[D / 32]) {
+  if (nv < KS) {   // kept as a real branch
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
@@ -159,7 +166,7 @@ __device__ __forceinline__ void softmax_tile(f32x16_t& s, int nv, int g2, float 
   float mx = fmaxf(s[0], s[1]);
 #pragma unroll
   for (int rr = 2; rr < 16; rr += 2) mx = fmaxf(mx, fmaxf(s[rr], s[rr + 1]));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  mx = fmaxf(mx, other_half(mx));
   // Lazy rescale: the running max moves only when some row max exceeds it
   // by more than 2^LAZY_LOG2; otherwise p <= 2^LAZY_LOG2 stays exact enough
   // in bf16 and the O/l rescale is skipped for the whole wave.
@@ -171,24 +178,11 @@ __device__ __forceinline__ void softmax_tile(f32x16_t& s, int nv, int g2, float 
     l_run *= alpha;
     m_run = m_new;
   }
-  const float mb = m_run * scale_log2;
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    f32x8_t pf;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) pf[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * m + t], scale_log2, -mb));
-    pb[m] = __builtin_convertvector(pf, bf16x8_t);
-#pragma unroll
-    for (int t = 0; t < 8; t += 2) {
-      const bf16x2_t pr = {pb[m][t], pb[m][t + 1]};
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
-    }
-  }
+  return m_run * scale_log2;
 }
 
 template <int D>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2 / NT, 2 / NT))) void attn_bf16_kernel(
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     DGeo g, float scale_log2) {
@@ -341,95 +335,67 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2 / NT,
     }
   }
 
-  // Prologue: stages 0..2 issued into buffers 0..2; stages 0 and 1 waited for.
-  int nv0 = 0, nv1 = 0, nv2 = 0;
+  // Prologue: stages 0 and 1 issued into buffers 0 and 1.
+  int nv0 = 0, nv1 = 0;
   VSA_LOAD_STAGE(0, nv0);
   VSA_LOAD_STAGE(1, nv1);
-  VSA_LOAD_STAGE(2, nv2);
-  __builtin_amdgcn_s_waitcnt(0);   // all of this wave's loads
-  __syncthreads();
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  f32x16_t s_cur[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) s_cur[t] = f32x16_t{};
-  if (ntiles > 0 && nv0 > 0) {
-    const uint8_t* kt = lds;
-    u32x4_t kfr[D / 16];
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) kfr[ks] = *reinterpret_cast<const u32x4_t*>(kt + kaddr[ks]);
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-      if (t < ntiles)
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-          s_cur[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kfr[ks]), qf[t][ks], s_cur[t], 0, 0, 0);
-  }
-
-  // Iteration t: softmax and PV of stage t (buffer t%4), QK of stage t+1,
-  // stage t+3 issued into buffer (t+3)%4 (last read by PV(t-1), which every
-  // wave finished before this iteration's barrier).  The loop is unrolled
-  // over the ring so buffer offsets are constants and the two S^T register
-  // sets swap roles instead of being copied.
-#define VSA_ITER(BC, S_CUR, S_NXT)                                                            \
+  // Iteration t: QK, softmax and PV of stage t (buffer t%3) while stages
+  // t+1 and t+2 are in flight; stage t+2 goes into buffer (t+2)%3, last read
+  // in iteration t-1, which every wave finished before this iteration's
+  // barrier.  Three workgroups share a compute unit, so other waves fill
+  // the matrix cores while one runs its softmax.  The loop is unrolled over
+  // the ring so buffer offsets are constants.
+#define VSA_ITER(BC)                                                                          \
   {                                                                                           \
-    /* Stage t+1 was issued two iterations ago: all but one stage of this */                  \
-    /* wave's loads are complete; the barrier makes every wave's visible. */                  \
-    if (nv2 > 0) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * C::IPW));                           \
+    /* This wave's loads of stage t are complete (stage t+1's may still be */                 \
+    /* in flight); the barrier makes every wave's visible. */                                 \
+    if (nv1 > 0) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * C::IPW));                           \
     else __builtin_amdgcn_s_waitcnt(0x0F70);                                                  \
     __syncthreads();                                                                          \
-    int nv3 = 0;                                                                              \
-    VSA_LOAD_STAGE(((BC) + 3) & 3, nv3);                                                      \
+    int nv2 = 0;                                                                              \
+    VSA_LOAD_STAGE(((BC) + 2) % NBUF, nv2);                                                   \
     if (ntiles > 0) {                                                                         \
-      const uint8_t* kt = lds + (((BC) + 1) & 3) * 2 * C::TILE_BYTES;                         \
-      if (nv1 > 0) {                                                                          \
-        u32x4_t kfr[D / 16];                                                                  \
-        _Pragma("unroll") for (int ks = 0; ks < D / 16; ++ks)                                  \
-          kfr[ks] = *reinterpret_cast<const u32x4_t*>(kt + kaddr[ks]);                        \
-        __builtin_amdgcn_sched_barrier(0);                                                    \
-        _Pragma("unroll") for (int t = 0; t < NT; ++t)                                         \
-          if (t < ntiles) {                                                                   \
-            S_NXT[t] = f32x16_t{};                                                            \
-            _Pragma("unroll") for (int ks = 0; ks < D / 16; ++ks)                              \
-              S_NXT[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                             \
-                  __builtin_bit_cast(bf16x8_t, kfr[ks]), qf[t][ks], S_NXT[t], 0, 0, 0);       \
-          }                                                                                   \
+      const uint8_t* kt = lds + (BC) * 2 * C::TILE_BYTES;                                     \
+      const uint8_t* vt = kt + C::TILE_BYTES;                                                 \
+      f32x16_t s = f32x16_t{};                                                                \
+      _Pragma("unroll") for (int ks = 0; ks < D / 16; ++ks) {                                  \
+        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kt + kaddr[ks]);                 \
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf), qf[0][ks], s, 0, 0, 0); \
       }                                                                                       \
-      __builtin_amdgcn_sched_barrier(0);                                                      \
-      const uint8_t* vt = lds + (BC) * 2 * C::TILE_BYTES + C::TILE_BYTES;                     \
-      i16x4_t vfr[2][2][D / 32];                                                              \
-      _Pragma("unroll") for (int m = 0; m < 2; ++m)                                            \
-        _Pragma("unroll") for (int hi = 0; hi < 2; ++hi)                                       \
-          _Pragma("unroll") for (int c = 0; c < D / 32; ++c)                                   \
-            vfr[m][hi][c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(                          \
-                (lds_i16x4_t*)(vt + vaddr[hi][c] + m * 16 * PARTS * 16));                     \
-      _Pragma("unroll") for (int t = 0; t < NT; ++t) {                                         \
-        if (t < ntiles) {                                                                     \
-          bf16x8_t pb[2];                                                                     \
-          softmax_tile<D>(S_CUR[t], nv0, g2, scale_log2, tau, m_run[t], l_run[t], acc[t], pb); \
-          _Pragma("unroll") for (int m = 0; m < 2; ++m)                                        \
-            _Pragma("unroll") for (int c = 0; c < D / 32; ++c) {                               \
-              const i16x8_t both = __builtin_shufflevector(vfr[m][0][c], vfr[m][1][c], 0, 1, 2, 3, 4, 5, 6, 7); \
-              acc[t][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                            \
-                  __builtin_bit_cast(bf16x8_t, both), pb[m], acc[t][c], 0, 0, 0);             \
-            }                                                                                 \
+      const float mb = softmax_prep<D>(s, nv0, g2, scale_log2, tau, m_run[0], l_run[0], acc[0]); \
+      _Pragma("unroll") for (int m = 0; m < 2; ++m) {                                          \
+        f32x8_t pf;                                                                           \
+        _Pragma("unroll") for (int q8 = 0; q8 < 8; ++q8)                                       \
+          pf[q8] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * m + q8], scale_log2, -mb));    \
+        const bf16x8_t pb = __builtin_convertvector(pf, bf16x8_t);                            \
+        _Pragma("unroll") for (int q8 = 0; q8 < 8; q8 += 2) {                                  \
+          const bf16x2_t pr = {pb[q8], pb[q8 + 1]};                                           \
+          l_run[0] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run[0], false);              \
+        }                                                                                     \
+        _Pragma("unroll") for (int c = 0; c < D / 32; ++c) {                                   \
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(                         \
+              (lds_i16x4_t*)(vt + vaddr[0][c] + m * 16 * PARTS * 16));                        \
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(                         \
+              (lds_i16x4_t*)(vt + vaddr[1][c] + m * 16 * PARTS * 16));                        \
+          const i16x8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);       \
+          acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                                \
+              __builtin_bit_cast(bf16x8_t, both), pb, acc[0][c], 0, 0, 0);                    \
         }                                                                                     \
       }                                                                                       \
     }                                                                                         \
-    nv0 = nv1; nv1 = nv2; nv2 = nv3;                                                          \
+    nv0 = nv1; nv1 = nv2;                                                                     \
   }
 
-  f32x16_t s_b[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) s_b[t] = f32x16_t{};
+  static_assert(NBUF == 3, "the loop below is unrolled over a three-stage ring");
   while (true) {
     if (nv0 == 0) break;
-    VSA_ITER(0, s_cur, s_b);
+    VSA_ITER(0);
     if (nv0 == 0) break;
-    VSA_ITER(1, s_b, s_cur);
+    VSA_ITER(1);
     if (nv0 == 0) break;
-    VSA_ITER(2, s_cur, s_b);
-    if (nv0 == 0) break;
-    VSA_ITER(3, s_b, s_cur);
+    VSA_ITER(2);
   }
 #undef VSA_ITER
 #undef VSA_LOAD_STAGE
