@@ -252,7 +252,7 @@ def main():
         "executed_tflop": round(flops / 1e12, 4),
         "issued_tflop_32x32_tiles": round(pflops / 1e12, 4),
         "nnz_blocks": int(rp[-1]),
-        "gpu": torch.cuda.get_device_name(0),
+        "gpu": torch.cuda.get_device_name(0) or torch.cuda.get_device_properties(0).gcnArchName,
     }
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
