@@ -5,9 +5,13 @@
 // the gather into the blocked layout is fused into the loads).
 //
 // bf16 path.  One workgroup of 4 waves per (batch*head, query block); wave w
-// owns query tokens [32w, 32w+32) of the block.  Per 64-key stage:
+// owns query tokens [32w, 32w+32) of the block; two workgroups share a
+// compute unit (two waves per SIMD, up to 256 VGPRs each).  The kept key
+// blocks of the row are cut into 32-key tiles (a block of n tokens gives
+// ceil(n/32) tiles) and walked in stages of two consecutive tiles, which may
+// come from two blocks.  Per tile:
 //   S^T (keys x queries) = K Q^T     on v_mfma_f32_32x32x16_bf16, Q in VGPRs,
-//                                    K from LDS ([key][d], padded rows)
+//                                    K from LDS (two 32-key tiles)
 //   online softmax in float32        the lane owns one query column, so the
 //                                    row max/sum are in-lane plus one swap
 //                                    with the lane 32 away
@@ -15,9 +19,14 @@
 //                                    V tile with the transposing LDS read,
 //                                    P^T straight from the S^T accumulators
 //                                    (same lane, same keys)
-// K/V stages are loaded into registers one stage ahead through raw buffer
-// loads (out-of-range reads return zero), so global latency overlaps the
-// matrix work of the current stage.
+// Software pipeline at 32-key tile granularity: while a wave turns one
+// tile's scores into probabilities and accumulates them into O, it already
+// computes the scores of the next tile, so matrix and vector work of the
+// same wave interleave.  K and V stages arrive through direct-to-LDS buffer
+// loads (rows past a block's end read out of range and land as zeros) one
+// iteration ahead, double-buffered: the two 32-key K tiles of a stage live
+// in separate rings, so K(t+2) tile 0 and K(t+1) tile 1 can both be issued at
+// the top of iteration t, as soon as their slots are free.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -37,22 +46,17 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-constexpr int KS = 32;              // keys per stage
-constexpr int NBUF = 3;             // LDS ring: stage t (QK and PV), stages t+1 and t+2 landing
-#ifndef VSA_ATTN_NT
-#define VSA_ATTN_NT 1
-#endif
-constexpr int NT = VSA_ATTN_NT;     // 32-query MFMA tiles per wave
-constexpr int WAVES = 4 / NT;       // waves per workgroup: 128 query tokens in all
+constexpr int KS = 64;              // keys per stage
+constexpr int KT = KS / 32;         // 32-key S^T tiles per stage
+constexpr int WAVES = 4;            // waves per workgroup: 128 query tokens in all
 constexpr int THREADS = 64 * WAVES;
-constexpr int QPW = 32 * NT;        // query tokens per wave
 constexpr float LAZY_LOG2 = 8.0f;   // running max is only raised when a row max exceeds it by 2^8
 
 // LDS tiles hold token rows of D bf16 (PARTS 16-byte pieces) with no
 // padding; piece pc of row r sits at slot pc ^ swz(r) of the row.  The
 // swizzle keeps both fragment reads conflict-free: the K reads (16 lanes,
 // 16 rows, one piece) and the transposing V reads (32 lanes, 4 rows, 4
-// consecutive pieces).
+// consecutive pieces).  It depends on r mod 16 only.
 template <int PARTS>
 __device__ __forceinline__ int swz(int r) {
   if constexpr (PARTS == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
@@ -62,25 +66,17 @@ __device__ __forceinline__ int swz(int r) {
 template <int D>
 struct AttnCfg {
   static constexpr int PARTS = D / 8;                  // 16-byte pieces per token row
-  static constexpr int TILE_BYTES = KS * D * 2;        // one K or V stage tile
-  static constexpr int ROWS_PER_INST = 64 / PARTS;     // rows one wave instruction fills
-  static constexpr int IPW = KS / ROWS_PER_INST / WAVES;  // load instructions per wave per tensor
+  static constexpr int ROW = D * 2;                    // bytes per token row
+  static constexpr int TILE = KS * ROW;                // one K or V stage
+  static constexpr int ROWS_PER_INST = 64 / PARTS;     // rows one wave load instruction fills
+  static constexpr int IPW = KS / ROWS_PER_INST / WAVES;  // load instructions per wave per tile
+  static_assert(IPW >= 1 && IPW * ROWS_PER_INST * WAVES == KS, "stage rows must split evenly over the waves");
 };
-
-// Raw buffer descriptor: loads past `bytes` return zero instead of faulting.
-// The base address is made explicitly wave-uniform so the descriptor stays
-// in scalar registers.
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)bytes, 0x00020000);
-}
 
 __device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Raw buffer descriptor as four scalar dwords (base, num_records, flags).
+// Raw buffer descriptor as four scalar dwords (base, num_records, flags):
+// loads past num_records return zero instead of faulting.
 struct Rsrc4 {
   u32x4_t d;
 };
@@ -115,85 +111,111 @@ __device__ inline uint32_t lds_addr(const void* p) {
 
 __device__ inline uint32_t bf16_pair(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// The key block a CSR entry names, with everything the loaders need; all
-// fields are wave-uniform.
-struct KeyBlock {
-  int nj;            // tokens in the block
-  bool nominal;      // (h, w) extents are the nominal block's
-  uint32_t jbase;    // byte offset of the block's origin token in the head
-  TokenMap map;      // token index -> raster index (for the other blocks)
-};
-
-template <int D>
-__device__ __forceinline__ KeyBlock open_block(const DGeo& g, const int32_t* __restrict__ col_idx, int entry,
-                                               bool stage_rows) {
-  const int j = uniform(min(max(col_idx[entry], 0), g.NB - 1));   // a corrupt index cannot leave the head
-  const Box bj = block_box_fast(g, j);
-  KeyBlock kb;
-  kb.nj = uniform(bj.n());
-  kb.nominal = uniform(bj.eh == g.bh && bj.ew == g.bw && stage_rows) != 0;
-  kb.map.base = uniform((bj.t0 * g.H + bj.h0) * g.W + bj.w0);
-  kb.jbase = (uint32_t)kb.map.base * (D * 2);
-  if (!kb.nominal) kb.map.init(g, bj);   // the reciprocals are only needed off the fast path
-  return kb;
-}
-
-// Value of the same lane in the other half of the wave (lane ^ 32).
-__device__ __forceinline__ float other_half(float x) {
+// Column max over the two halves of the wave: lanes l and l^32 hold the
+// same query column (different keys); afterwards every lane has the max.
+__device__ __forceinline__ float half_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  // r[0]: lanes 32..63 now hold lanes 0..31; r[1]: lanes 0..31 hold lanes 32..63.
-  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+  // r[0] holds the lower half's value in both halves, r[1] the upper half's.
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// First half of the online-softmax step for one 32-key x 32-query tile of
-// S^T held by this lane (query column l32; 16 of the 32 keys): masks keys
-// past `nv` (a block's last, partial stage only), takes the row max and
-// applies the lazy rescale to the tile's O^T accumulators.  Returns the
-// exponent offset m*scale*log2(e).
+// One 32-key x 32-query tile of S^T from the K rows at kt (LDS).
 template <int D>
-__device__ __forceinline__ float softmax_prep(f32x16_t& s, int nv, int g2, float scale_log2, float tau,
-                                              float& m_run, float& l_run, f32x16_t (&acc)[D / 32]) {
-  if (nv < KS) {   // kept as a real branch
-    asm volatile("" ::: "memory");
+__device__ __forceinline__ f32x16_t qk_tile(const uint8_t* kt, const uint32_t (&kaddr)[D / 16],
+                                            const bf16x8_t (&qf)[D / 16]) {
+  f32x16_t s = f32x16_t{};
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int key = 8 * (rr >> 2) + 4 * g2 + (rr & 3);
-      s[rr] = key < nv ? s[rr] : -INFINITY;
-    }
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kt + kaddr[ks]);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf), qf[ks], s, 0, 0, 0);
   }
-  float mx = fmaxf(s[0], s[1]);
+  return s;
+}
+
+// Lane (l32, g2) holds, in register rr of S^T tile kt, key
+// 32*kt + 8*(rr/4) + 4*g2 + rr%4 of the stage; keys at or past nv get -inf.
+__device__ __forceinline__ void mask_tile(f32x16_t& s, int kt, int nv, int g2x4) {
 #pragma unroll
-  for (int rr = 2; rr < 16; rr += 2) mx = fmaxf(mx, fmaxf(s[rr], s[rr + 1]));
-  mx = fmaxf(mx, other_half(mx));
-  // Lazy rescale: the running max moves only when some row max exceeds it
-  // by more than 2^LAZY_LOG2; otherwise p <= 2^LAZY_LOG2 stays exact enough
-  // in bf16 and the O/l rescale is skipped for the whole wave.
-  if (__ballot(mx > m_run + tau) != 0ull) {
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) acc[c] *= alpha;
-    l_run *= alpha;
-    m_run = m_new;
+  for (int rr = 0; rr < 16; ++rr) {
+    const int thr = nv - (32 * kt + 8 * (rr >> 2) + (rr & 3));
+    s[rr] = g2x4 < thr ? s[rr] : -INFINITY;
   }
-  return m_run * scale_log2;
+}
+
+// Max of the 16 scores this lane holds in an S^T tile (a v_max3 tree).
+__device__ __forceinline__ float tile_max(const f32x16_t& s) {
+  const float a = fmaxf(fmaxf(s[0], s[1]), s[2]), b = fmaxf(fmaxf(s[3], s[4]), s[5]);
+  const float c = fmaxf(fmaxf(s[6], s[7]), s[8]), d = fmaxf(fmaxf(s[9], s[10]), s[11]);
+  const float e = fmaxf(fmaxf(s[12], s[13]), s[14]);
+  return fmaxf(fmaxf(fmaxf(a, b), c), fmaxf(fmaxf(d, e), s[15]));
+}
+
+// Probabilities of registers [8h, 8h+8) of an S^T tile, rounded to bf16 for
+// the PV product; the row sum takes the rounded values, so that it matches
+// what is multiplied.
+__device__ __forceinline__ bf16x8_t probs(const f32x16_t& s, int h, float sl2, float mb, float& l) {
+  f32x8_t pf;
+#pragma unroll
+  for (int q8 = 0; q8 < 8; ++q8) pf[q8] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h + q8], sl2, -mb));
+  const bf16x8_t pb = __builtin_convertvector(pf, bf16x8_t);
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int q8 = 0; q8 < 8; q8 += 2) {
+    const bf16x2_t pr = {pb[q8], pb[q8 + 1]};
+    l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
+  }
+  return pb;
+}
+
+// O^T += V^T P^T over the 16 keys of k-step m of a stage (keys 16m + [0, 16)
+// in the order the S^T registers hold them).
+template <int D>
+__device__ __forceinline__ void pv_step(const uint8_t* vt, const uint32_t (&vaddr)[2][D / 32], int m,
+                                        const bf16x8_t& pb, f32x16_t (&acc)[D / 32]) {
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vt + vaddr[0][c] + m * 16 * D * 2));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vt + vaddr[1][c] + m * 16 * D * 2));
+    const i16x8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, both), pb, acc[c], 0, 0, 0);
+  }
 }
 
 template <int D>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_bf16_kernel(
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     DGeo g, float scale_log2) {
   using C = AttnCfg<D>;
-  constexpr int PARTS = C::PARTS;
-  // [buffer][K tile, V tile]
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * 2 * C::TILE_BYTES];
+  constexpr int PARTS = C::PARTS, IPW = C::IPW, ROW = C::ROW, TILE = C::TILE;
+  constexpr int RPI = C::ROWS_PER_INST;
+  constexpr int RSTEP = WAVES * RPI;       // stage rows between a wave's consecutive load instructions
+  constexpr int HALF = TILE / 2;           // one 32-key K tile
+  constexpr int IPH = IPW / 2;             // load instructions per wave per 32-key tile
+  static_assert(RSTEP % 16 == 0, "the swizzle of a lane's rows must not depend on the instruction");
+  // LDS: K tile-0 ring (2 x HALF), K tile-1 ring (2 x HALF), V ring (2 x TILE).
+  constexpr int A0 = 0, B0 = 2 * HALF, V0 = 4 * HALF;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * TILE];
+  // Byte offset (raster token offset * ROW) of token u of a block from the
+  // block's origin, for the four (h, w) extent combinations a block can
+  // have (nominal or cut short at the grid edge in each of h and w).
+  __shared__ uint32_t tok_tbl[4 * VSA_MAX_BLOCK_TOKENS];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);   // wave-uniform, so per-wave branches stay scalar
-  const int l32 = lane & 31, g2 = lane >> 5;
+  const int l32 = lane & 31, g2 = lane >> 5, g2x4 = 4 * g2;
+
+  {
+    const int eh_edge = g.H - (g.nbh - 1) * g.bh, ew_edge = g.W - (g.nbw - 1) * g.bw;
+    for (int idx = tid; idx < 4 * VSA_MAX_BLOCK_TOKENS; idx += THREADS) {
+      const int type = idx / VSA_MAX_BLOCK_TOKENS, u = idx % VSA_MAX_BLOCK_TOKENS;
+      const uint32_t eh = (type & 1) ? eh_edge : g.bh, ew = (type & 2) ? ew_edge : g.bw;
+      const uint32_t ehw = eh * ew;
+      const uint32_t ut = u / ehw, rem = u - ut * ehw, uh = rem / ew, uw = rem - uh * ew;
+      // Entries past a block's token count are never used.
+      tok_tbl[idx] = ((ut * (uint32_t)g.H + uh) * (uint32_t)g.W + uw) * (uint32_t)ROW;
+    }
+  }
 
   // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
   // contiguous range of (head, query block) items so that neighbouring
@@ -214,102 +236,151 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
   const Rsrc4 vrs = make_rsrc4(v + head_off, head_bytes);
   const uint32_t lds0 = (uint32_t)uniform((int)lds_addr(lds));
 
-  // This wave's query tiles: tokens [QPW*wave + 32*t, +32) of the block.
-  const int ntiles = min(NT, max(0, (ni - QPW * wave + 31) / 32));   // wave-uniform
-  // Q^T fragments (B operand): query column l32 of tile t, channels 16*ks + 8*g2 + [0, 8).
-  bf16x8_t qf[NT][D / 16];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int qtok = QPW * wave + 32 * t + l32;
+  // This wave's queries: tokens [32*wave, +32) of the block (none past ni).
+  const bool active = uniform(32 * wave < ni) != 0;
+  // Q^T fragments (B operand): query column l32, channels 16*ks + 8*g2 + [0, 8).
+  bf16x8_t qf[D / 16];
+  {
+    const int qtok = 32 * wave + l32;
     const bool ok = qtok < ni;
     const uint16_t* qp = q + head_off + (size_t)(ok ? qmap(qtok) : 0) * D + g2 * 8;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       u32x4_t raw = ok ? *reinterpret_cast<const u32x4_t*>(qp + ks * 16) : u32x4_t{0u, 0u, 0u, 0u};
-      qf[t][ks] = __builtin_bit_cast(bf16x8_t, raw);
+      qf[ks] = __builtin_bit_cast(bf16x8_t, raw);
     }
   }
 
-  f32x16_t acc[NT][D / 32];
+  f32x16_t acc[D / 32];
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) acc[t][c] = f32x16_t{};
-  float m_run[NT], l_run[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) { m_run[t] = -INFINITY; l_run[t] = 0.0f; }
+  for (int c = 0; c < D / 32; ++c) acc[c] = f32x16_t{};
+  float m_run = -INFINITY, l_run = 0.0f;
   const float tau = LAZY_LOG2 / scale_log2;
 
+  // Loader role.  Load instruction n of this wave covers stage row
+  // lrow + n*RSTEP (lane L: lrow = wave*RPI + L/PARTS, 16-byte slot
+  // L%PARTS, which holds piece (L%PARTS) ^ swz(row) of that key's token
+  // row): instructions n < IPH fill K tile 0, the others K tile 1, and all
+  // of them the V stage.
+  const int lrow = wave * RPI + lane / PARTS;
+  const uint32_t lpiece = (uint32_t)(((lane % PARTS) ^ swz<PARTS>(lrow)) * 16);
+
+  // Loader cursor (wave-uniform): the next 32-key tile to fetch is tokens
+  // [c_ld, c_ld + 32) of entry e_ld, a block with nj tokens, origin byte
+  // offset jbase and extent type ltype (a byte offset into tok_tbl).  A
+  // stage is two consecutive tiles of the row's tile sequence, so a stage
+  // may take its tiles from two blocks (of at most 32 tokens each).  The
+  // block ids of the next two entries are fetched ahead into jn1/jn2 by
+  // vector loads; a block is opened at least one iteration after its id
+  // was requested, so the iteration's wait has already covered the load.
   const int row = bh * g.NB + i;
   const int e_end = uniform(row_ptr[row + 1]);
   int e_ld = uniform(row_ptr[row]);
+  const __amdgpu_buffer_rsrc_t cirs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)col_idx, (short)0, e_end * 4, 0x00020000);
+  int c_ld = 0, nj = 0;
+  uint32_t jbase = 0, ltype = 0;
+  int jn1 = 0, jn2 = 0;
 
-  // Loader role.  Load instruction n of this wave fills slots
-  // [64*(wave*IPW + n), +64) of a tile: lane L writes row
-  // r_n = (wave*IPW + n)*ROWS_PER_INST + L/PARTS, slot L%PARTS, which holds
-  // piece (L%PARTS) ^ swz(r_n) of that key's token row.  When a stage spans
-  // whole rows of the nominal box (KS a multiple of bw, and KS and bh*bw
-  // multiples of one another) the source offset inside a nominal block is
-  // the offset in the first stage plus a wave-uniform step per stage.
-  const int nom_hw = g.bh * g.bw;
-  const bool stage_rows = (KS % g.bw == 0) && (KS % nom_hw == 0 || nom_hw % KS == 0);
-  // Offset of each 32-key stage slot of a nominal block from its origin.
-  uint32_t slot_off[4];
-#pragma unroll
-  for (int sl = 0; sl < 4; ++sl) {
-    const int u = sl * KS, ut = u / nom_hw, uh = (u - ut * nom_hw) / g.bw;
-    slot_off[sl] = (uint32_t)uniform((ut * g.H + uh) * g.W * D * 2);
-  }
-  int ld_row[C::IPW];
-  uint32_t ld_piece[C::IPW], ld_rel[C::IPW];
-#pragma unroll
-  for (int n = 0; n < C::IPW; ++n) {
-    const int r = (wave * C::IPW + n) * C::ROWS_PER_INST + lane / PARTS;
-    ld_row[n] = r;
-    ld_piece[n] = (uint32_t)(((lane % PARTS) ^ swz<PARTS>(r)) * 16);
-    const int ut = r / nom_hw, rr = r - ut * nom_hw;
-    const int uh = rr / g.bw, uw = rr - uh * g.bw;
-    ld_rel[n] = (uint32_t)((ut * g.H * g.W + uh * g.W + uw) * D * 2) + ld_piece[n];
-  }
-
-  // Loader cursor: the next stage to fetch is (entry e_ld, tokens from c_ld).
-  int c_ld = 0;
-  KeyBlock blk;
-  blk.nj = 0;
-  if (e_ld < e_end) blk = open_block<D>(g, col_idx, e_ld, stage_rows);
-
-  // Issue the stage at the cursor as direct-to-LDS loads into buffer BUF and
-  // advance; NV receives its valid key count (0 when the row is exhausted).
-  // Rows past the block's end read out of range and land as zeros.
-#define VSA_LOAD_STAGE(BUF, NV)                                                               \
+#define VSA_OPEN_BLOCK(JRAW)                                                                  \
   do {                                                                                        \
-    if (e_ld < e_end) {                                                                       \
-      const int nv_ = uniform(min(KS, blk.nj - c_ld));                                        \
-      const bool fast_ = blk.nominal;                                                         \
-      const int sl_ = c_ld >> 5;                                                              \
-      const uint32_t step_ = blk.jbase + (sl_ == 0 ? slot_off[0] : sl_ == 1 ? slot_off[1]     \
-                                           : sl_ == 2 ? slot_off[2] : slot_off[3]);           \
-      const uint32_t kt_ = (uint32_t)uniform((int)(lds0 + (BUF) * 2 * C::TILE_BYTES + wave * C::IPW * 1024)); \
-      _Pragma("unroll") for (int n = 0; n < C::IPW; ++n) {                                     \
-        uint32_t off = fast_ ? step_ + ld_rel[n]                                              \
-                             : (uint32_t)blk.map(c_ld + ld_row[n]) * (D * 2) + ld_piece[n];   \
-        off = ld_row[n] < nv_ ? off : 0x80000000u;                                            \
-        dma16(krs, kt_ + n * 1024, off);                                                      \
-        dma16(vrs, kt_ + C::TILE_BYTES + n * 1024, off);                                      \
+    const int j_ = uniform(min(max((JRAW), 0), g.NB - 1)); /* a corrupt id stays in the head */ \
+    const Box b_ = block_box_fast(g, j_);                                                     \
+    nj = uniform(b_.n());                                                                     \
+    jbase = (uint32_t)uniform(((b_.t0 * g.H + b_.h0) * g.W + b_.w0) * ROW);                   \
+    ltype = (uint32_t)uniform(((b_.eh != g.bh ? 1 : 0) | (b_.ew != g.bw ? 2 : 0)) *            \
+                              VSA_MAX_BLOCK_TOKENS * 4);                                      \
+  } while (0)
+
+  // Advance the cursor by one tile, opening the next block when this one is
+  // exhausted.
+#define VSA_ADVANCE()                                                                         \
+  do {                                                                                        \
+    c_ld = uniform(c_ld + 32);                                                                \
+    if (c_ld >= nj) {                                                                         \
+      c_ld = 0;                                                                               \
+      e_ld = uniform(e_ld + 1);                                                               \
+      if (e_ld < e_end) {                                                                     \
+        VSA_OPEN_BLOCK(__builtin_amdgcn_readfirstlane(jn1));                                  \
+        jn1 = jn2;                                                                            \
+        if (e_ld + 2 < e_end) jn2 = __builtin_amdgcn_raw_buffer_load_b32(cirs, (e_ld + 2) * 4, 0, 0); \
       }                                                                                       \
-      (NV) = nv_;                                                                             \
-      c_ld = uniform(c_ld + KS);                                                              \
-      if (c_ld >= blk.nj) {                                                                   \
-        c_ld = 0;                                                                             \
-        e_ld = uniform(e_ld + 1);                                                             \
-        if (e_ld < e_end) blk = open_block<D>(g, col_idx, e_ld, stage_rows);                  \
-      }                                                                                       \
-    } else {                                                                                  \
-      (NV) = 0;                                                                               \
     }                                                                                         \
   } while (0)
 
-  // Per-lane fragment byte offsets within a stage's tiles.
+  // Per-lane source offsets of the stage at the cursor (two tiles): the
+  // table reads are issued first, then PRE runs (DMA issue that does not
+  // depend on them), then the offsets are formed into OFF; the tiles' valid
+  // key counts go to NV0 and NV1 (0 for a tile past the row's end) and the
+  // cursor advances by the tiles taken.
+#define VSA_NEXT_STAGE(NV0, NV1, OFF, PRE)                                                    \
+  do {                                                                                        \
+    if (e_ld < e_end) {                                                                       \
+      uint32_t t_[IPW];                                                                       \
+      const int nv0_ = uniform(min(32, nj - c_ld));                                           \
+      const uint32_t jb0_ = jbase;                                                            \
+      {                                                                                       \
+        const uint8_t* tp_ = reinterpret_cast<const uint8_t*>(tok_tbl) + ltype + c_ld * 4;   \
+        _Pragma("unroll") for (int n = 0; n < IPH; ++n)                                        \
+          t_[n] = *reinterpret_cast<const uint32_t*>(tp_ + (lrow + n * RSTEP) * 4);           \
+      }                                                                                       \
+      VSA_ADVANCE();                                                                          \
+      int nv1_ = 0;                                                                           \
+      uint32_t jb1_ = 0;                                                                      \
+      if (e_ld < e_end) {                                                                     \
+        nv1_ = uniform(min(32, nj - c_ld));                                                   \
+        jb1_ = jbase;                                                                         \
+        const uint8_t* tp_ = reinterpret_cast<const uint8_t*>(tok_tbl) + ltype + c_ld * 4;   \
+        _Pragma("unroll") for (int n = IPH; n < IPW; ++n)                                      \
+          t_[n] = *reinterpret_cast<const uint32_t*>(tp_ + (lrow + n * RSTEP - 32) * 4);      \
+        VSA_ADVANCE();                                                                        \
+      }                                                                                       \
+      PRE;                                                                                    \
+      _Pragma("unroll") for (int n = 0; n < IPH; ++n) (OFF)[n] = jb0_ + t_[n] + lpiece;        \
+      if (nv0_ < 32) {                                                                        \
+        _Pragma("unroll") for (int n = 0; n < IPH; ++n)                                        \
+          (OFF)[n] = lrow < nv0_ - n * RSTEP ? (OFF)[n] : 0x80000000u;                        \
+      }                                                                                       \
+      if (nv1_ > 0) {                                                                         \
+        _Pragma("unroll") for (int n = IPH; n < IPW; ++n) (OFF)[n] = jb1_ + t_[n] + lpiece;    \
+        if (nv1_ < 32) {                                                                      \
+          _Pragma("unroll") for (int n = IPH; n < IPW; ++n)                                    \
+            (OFF)[n] = lrow < nv1_ - (n * RSTEP - 32) ? (OFF)[n] : 0x80000000u;               \
+        }                                                                                     \
+      } else {                                                                                \
+        _Pragma("unroll") for (int n = IPH; n < IPW; ++n) (OFF)[n] = 0x80000000u;              \
+      }                                                                                       \
+      (NV0) = nv0_;                                                                           \
+      (NV1) = nv1_;                                                                           \
+    } else {                                                                                  \
+      PRE;                                                                                    \
+      (NV0) = 0;                                                                              \
+      (NV1) = 0;                                                                              \
+    }                                                                                         \
+  } while (0)
+
+  // Direct-to-LDS issue: K tile 0 / K tile 1 / V of a stage with offsets OFF
+  // into the slot at LDS byte SLOT.
+#define VSA_ISSUE_K0(SLOT, OFF)                                                               \
+  do {                                                                                        \
+    const uint32_t base_ = (uint32_t)uniform((int)(lds0 + (SLOT) + wave * 1024));             \
+    _Pragma("unroll") for (int n = 0; n < IPH; ++n)                                            \
+      dma16(krs, base_ + n * WAVES * 1024, (OFF)[n]);                                         \
+  } while (0)
+#define VSA_ISSUE_K1(SLOT, OFF)                                                               \
+  do {                                                                                        \
+    const uint32_t base_ = (uint32_t)uniform((int)(lds0 + (SLOT) + wave * 1024));             \
+    _Pragma("unroll") for (int n = IPH; n < IPW; ++n)                                          \
+      dma16(krs, base_ + (n - IPH) * WAVES * 1024, (OFF)[n]);                                 \
+  } while (0)
+#define VSA_ISSUE_V(SLOT, OFF)                                                                \
+  do {                                                                                        \
+    const uint32_t base_ = (uint32_t)uniform((int)(lds0 + (SLOT) + wave * 1024));             \
+    _Pragma("unroll") for (int n = 0; n < IPW; ++n)                                            \
+      dma16(vrs, base_ + n * WAVES * 1024, (OFF)[n]);                                         \
+  } while (0)
+
+  // Per-lane fragment byte offsets within a tile.
   // K (A operand of S^T = K Q^T): row l32, piece 2*ks + g2.
   uint32_t kaddr[D / 16];
   {
@@ -335,76 +406,116 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
     }
   }
 
-  // Prologue: stages 0 and 1 issued into buffers 0 and 1.
-  int nv0 = 0, nv1 = 0;
-  VSA_LOAD_STAGE(0, nv0);
-  VSA_LOAD_STAGE(1, nv1);
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  __syncthreads();   // tok_tbl complete
+  if (e_ld < e_end) {
+    VSA_OPEN_BLOCK(col_idx[e_ld]);
+    if (e_ld + 1 < e_end) jn1 = __builtin_amdgcn_raw_buffer_load_b32(cirs, (e_ld + 1) * 4, 0, 0);
+    if (e_ld + 2 < e_end) jn2 = __builtin_amdgcn_raw_buffer_load_b32(cirs, (e_ld + 2) * 4, 0, 0);
+  }
 
-  // Iteration t: QK, softmax and PV of stage t (buffer t%3) while stages
-  // t+1 and t+2 are in flight; stage t+2 goes into buffer (t+2)%3, last read
-  // in iteration t-1, which every wave finished before this iteration's
-  // barrier.  Three workgroups share a compute unit, so other waves fill
-  // the matrix cores while one runs its softmax.  The loop is unrolled over
-  // the ring so buffer offsets are constants.
-#define VSA_ITER(BC)                                                                          \
+  // Prologue: all of stage 0 and K tile 0 of stage 1; S^T of stage 0 tile 0.
+  uint32_t offA[IPW], offB[IPW];
+  int nv0c = 0, nv1c = 0, nv0n = 0, nv1n = 0;   // valid keys of the tiles of stages t and t+1
+  VSA_NEXT_STAGE(nv0c, nv1c, offA, (void)0);
+  if (nv0c > 0) {
+    VSA_ISSUE_K0(A0, offA);
+    if (nv1c > 0) VSA_ISSUE_K1(B0, offA);
+    VSA_ISSUE_V(V0, offA);
+  }
+  VSA_NEXT_STAGE(nv0n, nv1n, offB, (void)0);
+  if (nv0n > 0) VSA_ISSUE_K0(A0 + HALF, offB);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __syncthreads();
+  f32x16_t sc, st;   // scores of the tile to exponentiate next / the tile after it
+  if (active && nv0c > 0) {
+    sc = qk_tile<D>(lds + A0, kaddr, qf);
+    if (nv0c < 32) mask_tile(sc, 0, nv0c, g2x4);
+    m_run = half_max(tile_max(sc));   // O and l are still zero: no rescale
+  }
+
+  // One 32-key tile step.  SC holds the scores of the tile whose V rows are
+  // at VT (its max is already folded into m_run): its probabilities go into
+  // O and l.  In the same block the scores of the next tile are computed
+  // from the K rows at KT into SN (unconditionally; when there is no next
+  // tile they are never used).  When HAS_NEXT, keys at or past NVN of that
+  // tile are masked and its max is folded into m_run; O and l are rescaled
+  // only when the max rose by more than 2^LAZY_LOG2 (a rare, wave-uniform
+  // branch after the pipelined block).
+#define VSA_STEP(SC, SN, VT, KT, HAS_NEXT, NVN)                                               \
   {                                                                                           \
-    /* This wave's loads of stage t are complete (stage t+1's may still be */                 \
-    /* in flight); the barrier makes every wave's visible. */                                 \
-    if (nv1 > 0) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * C::IPW));                           \
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                                                  \
-    __syncthreads();                                                                          \
-    int nv2 = 0;                                                                              \
-    VSA_LOAD_STAGE(((BC) + 2) % NBUF, nv2);                                                   \
-    if (ntiles > 0) {                                                                         \
-      const uint8_t* kt = lds + (BC) * 2 * C::TILE_BYTES;                                     \
-      const uint8_t* vt = kt + C::TILE_BYTES;                                                 \
-      f32x16_t s = f32x16_t{};                                                                \
-      _Pragma("unroll") for (int ks = 0; ks < D / 16; ++ks) {                                  \
-        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kt + kaddr[ks]);                 \
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf), qf[0][ks], s, 0, 0, 0); \
+    const float mb = m_run * scale_log2;                                                      \
+    __builtin_amdgcn_s_setprio(1); /* matrix-heavy block: win issue ties with the other wave */ \
+    SN = qk_tile<D>((KT), kaddr, qf);                                                         \
+    const bf16x8_t p0 = probs(SC, 0, scale_log2, mb, l_run);                                  \
+    const bf16x8_t p1 = probs(SC, 1, scale_log2, mb, l_run);                                  \
+    pv_step<D>((VT), vaddr, 0, p0, acc);                                                      \
+    pv_step<D>((VT), vaddr, 1, p1, acc);                                                      \
+    float mx = half_max(tile_max(SN)); /* right for a full tile; redone below otherwise */    \
+    __builtin_amdgcn_s_setprio(0);                                                            \
+    if (HAS_NEXT) {                                                                           \
+      const int nvn_ = (NVN);                                                                 \
+      if (nvn_ < 32) {                                                                        \
+        mask_tile(SN, 0, nvn_, g2x4);                                                         \
+        mx = half_max(tile_max(SN));                                                          \
       }                                                                                       \
-      const float mb = softmax_prep<D>(s, nv0, g2, scale_log2, tau, m_run[0], l_run[0], acc[0]); \
-      _Pragma("unroll") for (int m = 0; m < 2; ++m) {                                          \
-        f32x8_t pf;                                                                           \
-        _Pragma("unroll") for (int q8 = 0; q8 < 8; ++q8)                                       \
-          pf[q8] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * m + q8], scale_log2, -mb));    \
-        const bf16x8_t pb = __builtin_convertvector(pf, bf16x8_t);                            \
-        _Pragma("unroll") for (int q8 = 0; q8 < 8; q8 += 2) {                                  \
-          const bf16x2_t pr = {pb[q8], pb[q8 + 1]};                                           \
-          l_run[0] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run[0], false);              \
-        }                                                                                     \
-        _Pragma("unroll") for (int c = 0; c < D / 32; ++c) {                                   \
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(                         \
-              (lds_i16x4_t*)(vt + vaddr[0][c] + m * 16 * PARTS * 16));                        \
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(                         \
-              (lds_i16x4_t*)(vt + vaddr[1][c] + m * 16 * PARTS * 16));                        \
-          const i16x8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);       \
-          acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                                \
-              __builtin_bit_cast(bf16x8_t, both), pb, acc[0][c], 0, 0, 0);                    \
-        }                                                                                     \
+      if (__ballot(mx > m_run + tau) != 0ull) {                                               \
+        const float m_new = fmaxf(m_run, mx);                                                 \
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);             \
+        _Pragma("unroll") for (int c = 0; c < D / 32; ++c) acc[c] *= alpha;                    \
+        l_run *= alpha;                                                                       \
+        m_run = m_new;                                                                        \
       }                                                                                       \
     }                                                                                         \
-    nv0 = nv1; nv1 = nv2;                                                                     \
   }
 
-  static_assert(NBUF == 3, "the loop below is unrolled over a three-stage ring");
-  while (true) {
-    if (nv0 == 0) break;
-    VSA_ITER(0);
-    if (nv0 == 0) break;
-    VSA_ITER(1);
-    if (nv0 == 0) break;
-    VSA_ITER(2);
+  // Iteration t (P = t % 2).  Resident: K(t) tile 1 in B slot P, K(t+1)
+  // tile 0 in A slot 1-P, V(t) in V slot P, all issued an iteration earlier;
+  // sc holds the scores of stage t tile 0.  After the barrier every wave is
+  // done with iteration t-1, which last read A slot P (K(t) tile 0), B slot
+  // 1-P (K(t-1) tile 1) and V slot 1-P (V(t-1)): V(t+1), K(t+1) tile 1 and
+  // K(t+2) tile 0 go there.  A missing tile 1 (the row's last stage) reads
+  // stale LDS, fully masked.
+#define VSA_ITER(P, OFF_NEXT, OFF_NEW)                                                        \
+  {                                                                                           \
+    __builtin_amdgcn_s_waitcnt(0x0F70);                                                       \
+    __syncthreads();                                                                          \
+    int nv0nn = 0, nv1nn = 0;                                                                 \
+    VSA_NEXT_STAGE(nv0nn, nv1nn, OFF_NEW, {                                                   \
+      if (nv0n > 0) {                                                                         \
+        VSA_ISSUE_V(V0 + (1 - (P)) * TILE, OFF_NEXT);                                         \
+        if (nv1n > 0) VSA_ISSUE_K1(B0 + (1 - (P)) * HALF, OFF_NEXT);                          \
+      }                                                                                       \
+    });                                                                                       \
+    if (nv0nn > 0) VSA_ISSUE_K0(A0 + (P) * HALF, OFF_NEW);                                    \
+    if (active) {                                                                             \
+      const uint8_t* ka_ = lds + A0 + (1 - (P)) * HALF;   /* K(t+1) tile 0 */                 \
+      const uint8_t* kb_ = lds + B0 + (P) * HALF;         /* K(t) tile 1 */                   \
+      const uint8_t* v0_ = lds + V0 + (P) * TILE;         /* V(t) rows 0..31 */               \
+      VSA_STEP(sc, st, v0_, kb_, true, nv1c)                                                  \
+      VSA_STEP(st, sc, v0_ + 32 * ROW, ka_, nv0n > 0, nv0n)                                   \
+    }                                                                                         \
+    nv0c = nv0n; nv1c = nv1n;                                                                 \
+    nv0n = nv0nn; nv1n = nv1nn;                                                               \
+  }
+
+  while (nv0c > 0) {
+    VSA_ITER(0, offB, offA);
+    if (nv0c == 0) break;
+    VSA_ITER(1, offA, offB);
   }
 #undef VSA_ITER
-#undef VSA_LOAD_STAGE
+#undef VSA_STEP
+#undef VSA_ISSUE_V
+#undef VSA_ISSUE_K1
+#undef VSA_ISSUE_K0
+#undef VSA_NEXT_STAGE
+#undef VSA_OPEN_BLOCK
+#undef VSA_ADVANCE
 
   // Epilogue: O = O^T / l, rounded to bf16, stored at the query's raster row.
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const float l_tot = l_run[t] + __shfl_xor(l_run[t], 32, 64);
-    const int qtok = QPW * wave + 32 * t + l32;
+  {
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const int qtok = 32 * wave + l32;
     if (qtok < ni) {
       const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
       uint16_t* op = o + head_off + (size_t)qmap(qtok) * D;
@@ -414,8 +525,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
         for (int gq = 0; gq < 4; ++gq) {
           const int d = c * 32 + 8 * gq + 4 * g2;
           u32x2_t w;
-          w[0] = bf16_pair(f32_to_bf16(acc[t][c][4 * gq + 0] * inv), f32_to_bf16(acc[t][c][4 * gq + 1] * inv));
-          w[1] = bf16_pair(f32_to_bf16(acc[t][c][4 * gq + 2] * inv), f32_to_bf16(acc[t][c][4 * gq + 3] * inv));
+          w[0] = bf16_pair(f32_to_bf16(acc[c][4 * gq + 0] * inv), f32_to_bf16(acc[c][4 * gq + 1] * inv));
+          w[1] = bf16_pair(f32_to_bf16(acc[c][4 * gq + 2] * inv), f32_to_bf16(acc[c][4 * gq + 3] * inv));
           *reinterpret_cast<u32x2_t*>(op + d) = w;
         }
       }

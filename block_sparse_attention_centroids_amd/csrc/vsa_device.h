@@ -22,7 +22,7 @@ struct DGeo {
 
 // n / d with a precomputed magic (see DGeo); n and d below 2^16.
 __device__ inline int div_magic(int n, uint32_t magic) {
-  return magic == 0u ? n : (int)__umulhi((uint32_t)n, magic);
+  return magic == 0u ? n : (int)(((uint64_t)(uint32_t)n * magic) >> 32);
 }
 
 // Box of block j using the magic divisions (block ids are below 2^16).
