@@ -113,8 +113,7 @@ vsa_status vsa_plan(const void* q, const void* k, const vsa_shape* shape, const 
     index->nb = g.NB;
     index->window_t = window_t;
 
-    hipError_t e = launch_pool(q, shape->dtype, shape->D, qc, dg, BH, st_);
-    if (e == hipSuccess) e = launch_pool(k, shape->dtype, shape->D, kc, dg, BH, st_);
+    hipError_t e = launch_pool(q, qc, k, kc, shape->dtype, shape->D, dg, BH, st_);
     if (e == hipSuccess)
       e = launch_score_select(qc, kc, dg, shape->D, shape->heads, BH, sa, index->row_ptr,
                               index->col_idx, counts, bits, st_);
@@ -174,8 +173,8 @@ vsa_status vsa_centroids(const void* x, const vsa_shape* shape, float* out, void
   if (st != VSA_OK) return st;
   if (!x || !out || !aligned16(x) || !aligned16(out)) return VSA_ERR_INVALID_ARG;
   const Geo g = make_geo(*shape);
-  return hip_status(launch_pool(x, shape->dtype, shape->D, out, to_dgeo(g), shape->B * shape->heads,
-                                reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(launch_pool(x, out, nullptr, nullptr, shape->dtype, shape->D, to_dgeo(g),
+                                shape->B * shape->heads, reinterpret_cast<hipStream_t>(stream)));
 }
 
 vsa_status vsa_centroid_scores(const float* qc, const float* kc, const vsa_shape* shape, float* out,

@@ -18,73 +18,91 @@
 namespace vsa {
 
 // ---------------------------------------------------------------------------
-// Block means.  One wave per (tensor row bh, block j); lane c owns D/64
-// consecutive channels and walks the block's tokens in block order.
+// Block means.  One wave per (tensor, row bh, block j); lane c owns D/64
+// consecutive channels and walks the block's tokens in block order.  Token
+// offsets are stepped on the scalar unit and fed to the buffer loads as a
+// scalar offset, so a wave keeps PF token loads in flight; the adds stay in
+// token order.  Loads past the block's last token read out of range and
+// return +0, and adding +0 leaves a sum that started at +0 unchanged.
 // ---------------------------------------------------------------------------
+__device__ inline int uniform_i(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ inline __amdgpu_buffer_rsrc_t plan_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0,
+                                           (int)bytes, 0x00020000);
+}
+
+// One token's C channels for this lane, as float (bf16 widens exactly).
+template <typename T, int C>
+__device__ inline void load_token(__amdgpu_buffer_rsrc_t rs, int voff, int soff, float (&v)[C]) {
+  if constexpr (sizeof(T) == 2 && C == 2) {
+    const uint32_t two = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0);
+    v[0] = bf16_lo(two);
+    v[1] = bf16_hi(two);
+  } else if constexpr (sizeof(T) == 2) {
+    v[0] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rs, voff, soff, 0));
+  } else if constexpr (C == 2) {
+    const auto two = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0);
+    v[0] = __uint_as_float(two[0]);
+    v[1] = __uint_as_float(two[1]);
+  } else {
+    v[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0));
+  }
+}
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ x, float* __restrict__ out,
+__global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ x0, float* __restrict__ out0,
+                                                   const T* __restrict__ x1, float* __restrict__ out1,
                                                    DGeo g, int nitems) {
-  constexpr int C = D / 64;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int C = D / 64;   // channels per lane
+  constexpr int PF = 32;      // token loads in flight per wave
+  constexpr int ROWB = D * (int)sizeof(T);
+  const int wave = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int item = blockIdx.x * 4 + wave;
   if (item >= nitems) return;
+  const T* x = blockIdx.y ? x1 : x0;
+  float* out = blockIdx.y ? out1 : out0;
   const int bh = item / g.NB, j = item - bh * g.NB;
   const Box b = block_box(g, j);
-  const T* xb = x + (size_t)bh * g.N * D + lane * C;
+  const int n = uniform_i(b.n());
+  const __amdgpu_buffer_rsrc_t rs = plan_rsrc(x + (size_t)bh * g.N * D, (uint32_t)g.N * ROWB);
+  const int voff = lane * C * (int)sizeof(T);
+  // Scalar token cursor: byte offset of token u of the block, and its (h, w)
+  // position inside the box for stepping.
+  int soff = uniform_i(((b.t0 * g.H + b.h0) * g.W + b.w0) * ROWB);
+  int uh = 0, uw = 0;
+  const int ew = uniform_i(b.ew), eh = uniform_i(b.eh);
+  const int wrap_w = uniform_i((g.W - b.ew) * ROWB), wrap_h = uniform_i((g.H - b.eh) * g.W * ROWB);
   float acc[C];
 #pragma unroll
   for (int c = 0; c < C; ++c) acc[c] = 0.0f;
-  for (int ut = 0; ut < b.et; ++ut) {
-    for (int uh = 0; uh < b.eh; ++uh) {
-      const int row0 = ((b.t0 + ut) * g.H + (b.h0 + uh)) * g.W + b.w0;
-      const T* p = xb + (size_t)row0 * D;
-      int uw = 0;
-      // Loads are issued ahead in groups of 8; the adds stay in token order.
-      for (; uw + 8 <= b.ew; uw += 8) {
-        float v[8][C];
+  for (int u0 = 0; u0 < n; u0 += PF) {
+    float v[PF][C];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if constexpr (sizeof(T) == 2) {
-            if constexpr (C == 2) {
-              uint32_t two = *reinterpret_cast<const uint32_t*>(p + (size_t)(uw + e) * D);
-              v[e][0] = bf16_lo(two);
-              v[e][1] = bf16_hi(two);
-            } else {
-              v[e][0] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(p + (size_t)(uw + e) * D));
-            }
-          } else {
-#pragma unroll
-            for (int c = 0; c < C; ++c) v[e][c] = reinterpret_cast<const float*>(p)[(size_t)(uw + e) * D + c];
-          }
+    for (int e = 0; e < PF; ++e) {
+      load_token<T, C>(rs, voff, u0 + e < n ? soff : (int)0x80000000, v[e]);
+      // step to the next token of the box (row-major t, h, w)
+      soff += ROWB;
+      if (++uw == ew) {
+        uw = 0;
+        soff += wrap_w;
+        if (++uh == eh) {
+          uh = 0;
+          soff += wrap_h;
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-#pragma unroll
-          for (int c = 0; c < C; ++c) acc[c] = __fadd_rn(acc[c], v[e][c]);
-      }
-      for (; uw < b.ew; ++uw) {
-        float v[C];
-        if constexpr (sizeof(T) == 2) {
-          if constexpr (C == 2) {
-            uint32_t two = *reinterpret_cast<const uint32_t*>(p + (size_t)uw * D);
-            v[0] = bf16_lo(two);
-            v[1] = bf16_hi(two);
-          } else {
-            v[0] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(p + (size_t)uw * D));
-          }
-        } else {
-#pragma unroll
-          for (int c = 0; c < C; ++c) v[c] = reinterpret_cast<const float*>(p)[(size_t)uw * D + c];
-        }
-#pragma unroll
-        for (int c = 0; c < C; ++c) acc[c] = __fadd_rn(acc[c], v[c]);
       }
     }
+#pragma unroll
+    for (int e = 0; e < PF; ++e)
+#pragma unroll
+      for (int c = 0; c < C; ++c) acc[c] = __fadd_rn(acc[c], v[e][c]);
   }
-  const float n = (float)b.n();
   float* o = out + (size_t)item * D + lane * C;
 #pragma unroll
-  for (int c = 0; c < C; ++c) o[c] = __fdiv_rn(acc[c], n);
+  for (int c = 0; c < C; ++c) o[c] = __fdiv_rn(acc[c], (float)n);
 }
 
 // Scores of RT query blocks (rows i0..i0+RT-1, clamped) against key block j.
@@ -161,17 +179,42 @@ __global__ __launch_bounds__(256) void score_select_kernel(
   for (int r = wave; r < rows_here; r += 4) {
     const int i = i0 + r;
     const uint32_t* keys = smem + r * NB;
+    // k-th largest key, bit by bit from the top: thr grows to the largest
+    // value with at least kk keys >= thr.  Counts are ballots; rows of at
+    // most 512 blocks keep their keys in registers.
     uint32_t thr = 0u;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = thr | (1u << bit);
-      int cnt = 0;
-      for (int j = lane; j < NB; j += 64) cnt += keys[j] >= cand ? 1 : 0;
-      cnt = wave_sum(cnt);
-      if (cnt >= kk) thr = cand;
-    }
     int gt = 0;
-    for (int j = lane; j < NB; j += 64) gt += keys[j] > thr ? 1 : 0;
-    gt = wave_sum(gt);
+    if (NB <= 64 * 8) {
+      uint32_t kv[8];
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) {
+        const int j = s2 * 64 + lane;
+        kv[s2] = j < NB ? keys[j] : 0u;   // below every real key
+      }
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = thr | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) cnt += __popcll(__ballot(kv[s2] >= cand));
+        if (cnt >= kk) thr = cand;
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) gt += __popcll(__ballot(kv[s2] > thr));
+    } else {
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = thr | (1u << bit);
+        int cnt = 0;
+        for (int j0 = 0; j0 < NB; j0 += 64) {
+          const int j = j0 + lane;
+          cnt += __popcll(__ballot(j < NB && keys[j] >= cand));
+        }
+        if (cnt >= kk) thr = cand;
+      }
+      for (int j0 = 0; j0 < NB; j0 += 64) {
+        const int j = j0 + lane;
+        gt += __popcll(__ballot(j < NB && keys[j] > thr));
+      }
+    }
     const int need = kk - gt;   // >= 1 keys equal to thr are kept, lowest ids first
     const int tbi = i / per_t;
     const int64_t row = (int64_t)bh * NB + i;
@@ -271,26 +314,30 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ q
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_pool(const void* x, int dtype, int D, float* out, const DGeo& g, int BH,
-                       hipStream_t st) {
+hipError_t launch_pool(const void* x0, float* out0, const void* x1, float* out1, int dtype, int D,
+                       const DGeo& g, int BH, hipStream_t st) {
   const int nitems = BH * g.NB;
-  dim3 grid((nitems + 3) / 4), block(256);
+  dim3 grid((nitems + 3) / 4, x1 ? 2 : 1), block(256);
   if (dtype == 0) {
     if (D == 128)
-      hipLaunchKernelGGL((pool_kernel<uint16_t, 128>), grid, block, 0, st, (const uint16_t*)x, out, g, nitems);
+      hipLaunchKernelGGL((pool_kernel<uint16_t, 128>), grid, block, 0, st, (const uint16_t*)x0, out0,
+                         (const uint16_t*)x1, out1, g, nitems);
     else
-      hipLaunchKernelGGL((pool_kernel<uint16_t, 64>), grid, block, 0, st, (const uint16_t*)x, out, g, nitems);
+      hipLaunchKernelGGL((pool_kernel<uint16_t, 64>), grid, block, 0, st, (const uint16_t*)x0, out0,
+                         (const uint16_t*)x1, out1, g, nitems);
   } else {
     if (D == 128)
-      hipLaunchKernelGGL((pool_kernel<float, 128>), grid, block, 0, st, (const float*)x, out, g, nitems);
+      hipLaunchKernelGGL((pool_kernel<float, 128>), grid, block, 0, st, (const float*)x0, out0,
+                         (const float*)x1, out1, g, nitems);
     else
-      hipLaunchKernelGGL((pool_kernel<float, 64>), grid, block, 0, st, (const float*)x, out, g, nitems);
+      hipLaunchKernelGGL((pool_kernel<float, 64>), grid, block, 0, st, (const float*)x0, out0,
+                         (const float*)x1, out1, g, nitems);
   }
   return hipGetLastError();
 }
 
 int select_rows_per_block(int NB) {
-  // RT rows of NB uint32 keys must fit in 64 KiB of LDS.
+  // RT rows of NB uint32 keys must fit in 64 KiB of LDS (plus 4 KiB of query means).
   if (NB * 8 * 4 <= 65536) return 8;
   if (NB * 4 * 4 <= 65536) return 4;
   if (NB * 2 * 4 <= 65536) return 2;

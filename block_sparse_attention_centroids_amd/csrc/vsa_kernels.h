@@ -19,8 +19,9 @@ struct SelectArgs {
   int32_t words;                // 64-bit bitmap words per row
 };
 
-hipError_t launch_pool(const void* x, int dtype, int D, float* out, const DGeo& g, int BH,
-                       hipStream_t st);
+// Block means of x0 into out0 and, when x1 is not null, of x1 into out1.
+hipError_t launch_pool(const void* x0, float* out0, const void* x1, float* out1, int dtype, int D,
+                       const DGeo& g, int BH, hipStream_t st);
 hipError_t launch_score_select(const float* qc, const float* kc, const DGeo& g, int D, int heads,
                                int BH, const SelectArgs& sa, int32_t* row_ptr, int32_t* col_idx,
                                int32_t* counts, uint64_t* bits, hipStream_t st);
