@@ -254,6 +254,27 @@ def main():
         "nnz_blocks": int(rp[-1]),
         "gpu": torch.cuda.get_device_name(0) or torch.cuda.get_device_properties(0).gcnArchName,
     }
+    # Scheme generation (outside the timed step): head-wise blocking-scheme
+    # selection over three 128-token candidates; it reads Q and K once per
+    # candidate, so it is reported against the HBM roofline.
+    if w.dtype == "bf16" and w.D == 128 and w.name == "wan13b":
+        cands = [(4, 4, 8), (1, 8, 16), (2, 8, 8)]
+        for _ in range(3):
+            vsa.select_scheme(q, k, w.grid, cands)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            _, choice = vsa.select_scheme(q, k, w.grid, cands)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sel_ms = e0.elapsed_time(e1) / 10
+        sel_bytes = len(cands) * 2 * q.numel() * q.element_size()
+        result["scheme_select"] = {
+            "candidates": [list(c) for c in cands], "ms": round(sel_ms, 4),
+            "algorithmic_bytes": sel_bytes, "GB_per_s": round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(sel_bytes / (sel_ms * 1e-3) / 8e12, 4),
+            "choices": choice.cpu().tolist()}
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inp, w, rp, ci, sizes, flops, a.cpu_budget)

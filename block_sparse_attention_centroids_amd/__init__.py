@@ -24,7 +24,7 @@ from . import _lib
 from ._lib import VsaError, VsaIndex, VsaShape, check, load
 
 __all__ = ["plan", "attn", "query", "permute", "unpermute", "centroids", "centroid_scores",
-           "Index", "VsaError", "load"]
+           "sics", "select_scheme", "Index", "VsaError", "load"]
 
 _DTYPES = {torch.bfloat16: _lib.VSA_BF16, torch.float32: _lib.VSA_F32}
 
@@ -187,3 +187,39 @@ def centroid_scores(qc: torch.Tensor, kc: torch.Tensor, grid, block, dtype=torch
                                   ctypes.byref(s), ctypes.c_void_p(out.data_ptr()), _stream(qc)),
           "vsa_centroid_scores")
     return out
+
+
+def sics(x: torch.Tensor, grid, block) -> torch.Tensor:
+    """Intra-block aggregation (sum of pairwise cosine similarities) of every
+    block, float32 [B, heads, NB]."""
+    lib = load()
+    s = _shape_of(x, grid, block)
+    nb = math.prod(-(-int(n) // int(b)) for n, b in zip(grid, block))
+    out = torch.empty((s.B, s.heads, nb), dtype=torch.float32, device=x.device)
+    check(lib.vsa_sics(ctypes.c_void_p(x.data_ptr()), ctypes.byref(s), ctypes.c_void_p(out.data_ptr()),
+                       _stream(x)), "vsa_sics")
+    return out
+
+
+def select_scheme(q: torch.Tensor, k: torch.Tensor, grid, candidates: Sequence[Sequence[int]]):
+    """Head-wise blocking-scheme selection: returns (scores float32
+    [n_cand, B*heads] = AS(Q|c) + AS(K|c), choice int32 [B*heads])."""
+    lib = load()
+    s = _shape_of(q, grid, candidates[0])
+    if k.shape != q.shape or k.dtype != q.dtype or not k.is_contiguous():
+        raise ValueError("k must match q")
+    flat = [int(a) for c in candidates for a in c]
+    if len(flat) != 3 * len(candidates):
+        raise ValueError("each candidate is a (bt, bh, bw) triple")
+    cand = (ctypes.c_int32 * len(flat))(*flat)
+    n = len(candidates)
+    wsb = ctypes.c_size_t()
+    check(lib.vsa_scheme_workspace(ctypes.byref(s), cand, n, ctypes.byref(wsb)), "vsa_scheme_workspace")
+    ws = torch.empty(max(int(wsb.value), 1), dtype=torch.uint8, device=q.device)
+    bh = s.B * s.heads
+    scores = torch.empty((n, bh), dtype=torch.float32, device=q.device)
+    choice = torch.empty((bh,), dtype=torch.int32, device=q.device)
+    check(lib.vsa_select_scheme(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.byref(s),
+                                cand, n, ctypes.c_void_p(scores.data_ptr()), ctypes.c_void_p(choice.data_ptr()),
+                                ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(q)), "vsa_select_scheme")
+    return scores, choice

@@ -41,7 +41,8 @@ class VsaError(RuntimeError):
 _lib = None
 
 EXPORTS = ("vsa_query", "vsa_plan", "vsa_attn", "vsa_permute", "vsa_unpermute",
-           "vsa_centroids", "vsa_centroid_scores", "vsa_status_str")
+           "vsa_centroids", "vsa_centroid_scores", "vsa_sics", "vsa_scheme_workspace",
+           "vsa_select_scheme", "vsa_status_str")
 
 
 def load() -> ctypes.CDLL:
@@ -67,6 +68,11 @@ def load() -> ctypes.CDLL:
     lib.vsa_unpermute.argtypes = [P, ctypes.POINTER(VsaShape), P, P]
     lib.vsa_centroids.argtypes = [P, ctypes.POINTER(VsaShape), P, P]
     lib.vsa_centroid_scores.argtypes = [P, P, ctypes.POINTER(VsaShape), P, P]
+    lib.vsa_sics.argtypes = [P, ctypes.POINTER(VsaShape), P, P]
+    lib.vsa_scheme_workspace.argtypes = [ctypes.POINTER(VsaShape), ctypes.POINTER(ctypes.c_int32), I,
+                                         ctypes.POINTER(ctypes.c_size_t)]
+    lib.vsa_select_scheme.argtypes = [P, P, ctypes.POINTER(VsaShape), ctypes.POINTER(ctypes.c_int32), I, P, P,
+                                      P, ctypes.c_size_t, P]
     for name in EXPORTS[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     lib.vsa_status_str.argtypes = [ctypes.c_int]

@@ -32,6 +32,7 @@ SOURCES = {
     # max/min need not quiet signalling NaNs.
     "attn.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
     "layout.hip": [],
+    "schemes.hip": [],
     "api.hip": [],
 }
 

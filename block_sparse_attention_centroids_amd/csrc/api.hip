@@ -187,4 +187,71 @@ vsa_status vsa_centroid_scores(const float* qc, const float* kc, const vsa_shape
                                   reinterpret_cast<hipStream_t>(stream)));
 }
 
+vsa_status vsa_sics(const void* x, const vsa_shape* shape, float* out, void* stream) {
+  vsa_status st = check_shape(shape);
+  if (st != VSA_OK) return st;
+  if (!x || !out || !aligned16(x)) return VSA_ERR_INVALID_ARG;
+  const Geo g = make_geo(*shape);
+  return hip_status(launch_sics(x, out, nullptr, nullptr, shape->dtype, shape->D, to_dgeo(g),
+                                shape->B * shape->heads, reinterpret_cast<hipStream_t>(stream)));
+}
+
+// Validates the candidates and lays out the workspace: per candidate the
+// block SICS of Q then K, each candidate's region 256-byte aligned.
+static vsa_status scheme_layout(const vsa_shape* shape, const int32_t* cand, int n_cand, vsa::SchemeArgs* sa,
+                                size_t* bytes) {
+  if (!shape || !cand || n_cand < 1 || n_cand > VSA_MAX_SCHEMES) return VSA_ERR_INVALID_ARG;
+  const int64_t BH = (int64_t)shape->B * shape->heads;
+  size_t off = 0;
+  for (int c = 0; c < n_cand; ++c) {
+    vsa_shape s = *shape;
+    s.bt = cand[3 * c];
+    s.bh = cand[3 * c + 1];
+    s.bw = cand[3 * c + 2];
+    const vsa_status st = check_shape(&s);
+    if (st != VSA_OK) return st;
+    const Geo g = make_geo(s);
+    if (sa) {
+      sa->nb[c] = g.NB;
+      sa->off[c] = (int64_t)(off / sizeof(float));
+    }
+    off = align256(off + (size_t)2 * BH * g.NB * sizeof(float));
+  }
+  if (sa) sa->n = n_cand;
+  if (bytes) *bytes = off;
+  return VSA_OK;
+}
+
+vsa_status vsa_scheme_workspace(const vsa_shape* shape, const int32_t* candidates, int n_cand,
+                                size_t* ws_bytes) {
+  return scheme_layout(shape, candidates, n_cand, nullptr, ws_bytes);
+}
+
+vsa_status vsa_select_scheme(const void* q, const void* k, const vsa_shape* shape, const int32_t* candidates,
+                             int n_cand, float* scores, int32_t* choice, void* ws, size_t ws_bytes,
+                             void* stream) {
+  vsa::SchemeArgs sa{};
+  size_t need = 0;
+  vsa_status st = scheme_layout(shape, candidates, n_cand, &sa, &need);
+  if (st != VSA_OK) return st;
+  if (!q || !k || !scores || !choice || !ws || !aligned16(q) || !aligned16(k) || !aligned16(ws))
+    return VSA_ERR_INVALID_ARG;
+  if (ws_bytes < need) return VSA_ERR_WORKSPACE;
+  hipStream_t st_ = reinterpret_cast<hipStream_t>(stream);
+  const int BH = shape->B * shape->heads;
+  float* sics = static_cast<float*>(ws);
+  for (int c = 0; c < n_cand; ++c) {
+    vsa_shape s = *shape;
+    s.bt = candidates[3 * c];
+    s.bh = candidates[3 * c + 1];
+    s.bw = candidates[3 * c + 2];
+    const Geo g = make_geo(s);
+    float* base = sics + sa.off[c];
+    const hipError_t e = launch_sics(q, base, k, base + (size_t)BH * g.NB, shape->dtype, shape->D,
+                                     to_dgeo(g), BH, st_);
+    if (e != hipSuccess) return VSA_ERR_HIP;
+  }
+  return hip_status(launch_scheme_select(sics, sa, BH, scores, choice, st_));
+}
+
 }  // extern "C"

@@ -19,6 +19,14 @@ struct SelectArgs {
   int32_t words;                // 64-bit bitmap words per row
 };
 
+// Per-candidate layout of the block SICS in the scheme workspace: candidate
+// c holds [2][BH][nb[c]] floats (Q, then K) starting at float offset off[c].
+struct SchemeArgs {
+  int32_t n;
+  int32_t nb[VSA_MAX_SCHEMES];
+  int64_t off[VSA_MAX_SCHEMES];
+};
+
 // Block means of x0 into out0 and, when x1 is not null, of x1 into out1.
 hipError_t launch_pool(const void* x0, float* out0, const void* x1, float* out1, int dtype, int D,
                        const DGeo& g, int BH, hipStream_t st);
@@ -33,6 +41,11 @@ hipError_t launch_scores(const float* qc, const float* kc, float* out, int NB, i
 hipError_t launch_attn(const void* q, const void* k, const void* v, void* o, int dtype, int D,
                        const int32_t* row_ptr, const int32_t* col_idx, const DGeo& g, int BH,
                        float scale, hipStream_t st);
+// Per-block SICS of x0 into out0 and, when x1 is not null, of x1 into out1.
+hipError_t launch_sics(const void* x0, float* out0, const void* x1, float* out1, int dtype, int D,
+                       const DGeo& g, int BH, hipStream_t st);
+hipError_t launch_scheme_select(const float* sics, const SchemeArgs& sa, int BH, float* scores,
+                                int32_t* choice, hipStream_t st);
 hipError_t launch_permute(const void* x, void* xb, int elt, int D, const DGeo& g, int BH, int P,
                           bool inverse, hipStream_t st);
 

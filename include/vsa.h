@@ -86,6 +86,8 @@ typedef struct {
 /* Largest supported head count with per-head densities, and block size. */
 #define VSA_MAX_HEADS 256
 #define VSA_MAX_BLOCK_TOKENS 128
+/* Largest number of blocking-scheme candidates vsa_select_scheme takes. */
+#define VSA_MAX_SCHEMES 16
 
 /* Host-only sizing query; touches no device.
  * density: host float[n_density], n_density = 1 (all heads) or heads; each
@@ -138,6 +140,32 @@ vsa_status vsa_centroids(const void* x, const vsa_shape* shape, float* out, void
  * [B, heads, NB, NB] with out[.., i, j] = <qc_i, kc_j> in vsa_plan's order. */
 vsa_status vsa_centroid_scores(const float* qc, const float* kc, const vsa_shape* shape,
                                float* out, void* stream);
+
+/* Intra-block aggregation (SPADE 3.2, Eq. 4-5 and Algorithm 1): for every
+ * block of shape's blocking, the sum of all pairwise cosine similarities of
+ * its token vectors, computed as the squared norm of the sum of the
+ * unit-normalized tokens in float32.  A cut-short edge block uses its own
+ * tokens; a zero token vector adds nothing.  x: device [B, heads, N, D];
+ * out: device float32 [B, heads, NB]. */
+vsa_status vsa_sics(const void* x, const vsa_shape* shape, float* out, void* stream);
+
+/* Workspace bytes vsa_select_scheme needs for these candidates (host only).
+ * candidates: host int32 [n_cand][3] block shapes (bt, bh, bw), 1 <= n_cand
+ * <= VSA_MAX_SCHEMES; each must be a valid blocking of shape's grid. */
+vsa_status vsa_scheme_workspace(const vsa_shape* shape, const int32_t* candidates, int n_cand,
+                                size_t* ws_bytes);
+
+/* Head-wise blocking-scheme selection (SPADE 3.2): the aggregation score of
+ * a candidate is the sum of its blocks' SICS (Eq. 3); a head's score is
+ * AS(Q | c) + AS(K | c) and it selects the first candidate with the highest
+ * score.  shape gives B, heads, D, grid and dtype (its block fields are not
+ * used).  q, k: device [B, heads, N, D]; scores: device float32
+ * [n_cand, B*heads]; choice: device int32 [B*heads] (candidate index);
+ * ws: device workspace of vsa_scheme_workspace bytes.  The sums run in a
+ * fixed order, so the choice is reproducible. */
+vsa_status vsa_select_scheme(const void* q, const void* k, const vsa_shape* shape,
+                             const int32_t* candidates, int n_cand, float* scores, int32_t* choice,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* vsa_status_str(vsa_status s);

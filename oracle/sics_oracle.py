@@ -56,16 +56,39 @@ def sics_online(xb: np.ndarray) -> float:
     return 2.0 * sigma + nonzero
 
 
-def block_sics(x: np.ndarray, g: "O.Geometry") -> np.ndarray:
+def _sics_online_many(xb: np.ndarray) -> np.ndarray:
+    """Algorithm 1 run side by side on many blocks of the same token count:
+    xb [m, n, d] -> [m], each block with exactly the steps of sics_online."""
+    xb = np.asarray(xb, dtype=np.float64)
+    m, n, d = xb.shape
+    r = np.zeros((m, d), dtype=np.float64)
+    sigma = np.zeros(m, dtype=np.float64)
+    nonzero = np.zeros(m, dtype=np.float64)
+    for t in range(n):
+        x = xb[:, t, :]
+        norm = np.sqrt(np.einsum("md,md->m", x, x))
+        ok = norm > 0.0
+        xh = np.where(ok[:, None], x / np.where(ok, norm, 1.0)[:, None], 0.0)
+        sigma += np.where(ok, np.einsum("md,md->m", r, xh), 0.0)
+        r += xh
+        nonzero += ok
+    return 2.0 * sigma + nonzero
+
+
+def block_sics(x: np.ndarray, g: "O.Geometry", heads: Sequence[int] = None) -> np.ndarray:
     """SICS of every block of x [B, heads, N, d] under the blocking of g:
     float64 [B, heads, NB], each block by Algorithm 1 over its tokens in
-    block order (R11)."""
+    block order (R11).  heads limits the work to some heads (the others
+    stay zero)."""
     B, Hh = x.shape[:2]
     out = np.zeros((B, Hh, g.NB), dtype=np.float64)
-    for b in range(B):
-        for h in range(Hh):
-            for j in range(g.NB):
-                out[b, h, j] = sics_online(x[b, h, g.tokens[j]])
+    hs = range(Hh) if heads is None else heads
+    for size in np.unique(g.sizes):
+        js = np.nonzero(g.sizes == size)[0]
+        idx = np.stack([g.tokens[j] for j in js])          # [m, size]
+        for b in range(B):
+            for h in hs:
+                out[b, h, js] = _sics_online_many(x[b, h][idx])
     return out
 
 

@@ -180,3 +180,27 @@ def test_magic_division_exact():
     for d in list(range(2, 300)) + [1176, 4096, 16383]:
         m = np.uint64(((1 << 32) + d - 1) // d)
         assert np.array_equal((n * m) >> np.uint64(32), n // np.uint64(d)), d
+
+
+def test_scheme_entry_error_paths(lib):
+    w = W.WORKLOADS["wan13b"]
+    shape = _shape(w)
+    good = (ctypes.c_int32 * 6)(4, 4, 8, 1, 8, 16)
+    ws = ctypes.c_size_t()
+    assert lib.vsa_scheme_workspace(ctypes.byref(shape), good, 2, ctypes.byref(ws)) == 0
+    g1, g2 = O.geometry(w.grid, (4, 4, 8)), O.geometry(w.grid, (1, 8, 16))
+    assert ws.value >= 2 * 12 * (g1.NB + g2.NB) * 4
+    assert lib.vsa_scheme_workspace(ctypes.byref(shape), good, 0, ctypes.byref(ws)) == _lib.VSA_ERR_INVALID_ARG
+    assert lib.vsa_scheme_workspace(ctypes.byref(shape), good, 17, ctypes.byref(ws)) == _lib.VSA_ERR_INVALID_ARG
+    too_big = (ctypes.c_int32 * 3)(8, 8, 8)     # 512-token blocks
+    assert lib.vsa_scheme_workspace(ctypes.byref(shape), too_big, 1, ctypes.byref(ws)) == _lib.VSA_ERR_UNSUPPORTED
+    zero = (ctypes.c_int32 * 3)(0, 4, 8)
+    assert lib.vsa_scheme_workspace(ctypes.byref(shape), zero, 1, ctypes.byref(ws)) == _lib.VSA_ERR_INVALID_ARG
+    out = FAKE
+    assert lib.vsa_select_scheme(FAKE, FAKE, ctypes.byref(shape), good, 2, out, out, FAKE, ws.value - 1,
+                                 None) == _lib.VSA_ERR_WORKSPACE
+    assert lib.vsa_select_scheme(None, FAKE, ctypes.byref(shape), good, 2, out, out, FAKE, ws.value,
+                                 None) == _lib.VSA_ERR_INVALID_ARG
+    assert lib.vsa_sics(None, ctypes.byref(shape), FAKE, None) == _lib.VSA_ERR_INVALID_ARG
+    bad = VsaShape(1, 1, 96, 4, 8, 8, 2, 4, 8, 0)
+    assert lib.vsa_sics(FAKE, ctypes.byref(bad), FAKE, None) == _lib.VSA_ERR_UNSUPPORTED

@@ -116,3 +116,14 @@ def test_selection_prefers_the_scheme_that_follows_the_structure():
 def test_selection_ties_go_to_the_lowest_index():
     sc = np.array([[[1.0, 3.0]], [[2.0, 3.0]], [[2.0, 1.0]]])   # [cand, B, heads]
     assert S.select_scheme(sc).tolist() == [[1, 0]]
+
+
+def test_vectorized_blocks_match_one_block_at_a_time():
+    grid, block = (5, 6, 7), (2, 4, 4)
+    g = O.geometry(grid, block)
+    x = np.random.default_rng(10).standard_normal((1, 2, int(np.prod(grid)), 8))
+    x[0, 1, 3] = 0.0
+    bs = S.block_sics(x, g)
+    for h in range(2):
+        for j in range(g.NB):
+            assert bs[0, h, j] == pytest.approx(S.sics_online(x[0, h, g.tokens[j]]), rel=1e-12, abs=1e-12)
