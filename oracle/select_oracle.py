@@ -21,7 +21,10 @@ Readings where the pages are silent (also listed in the design notes):
   scores times the logit scale (1/sqrt(d) unless given):
   prob_j = exp(scale*s_j) / sum_l exp(scale*s_l).  It keeps the shortest
   prefix of the row, taken in (score descending, block id ascending) order,
-  whose cumulative probability is at least p: at least one block, and the
+  whose cumulative probability is at least p: at least one block.  p = 1
+  keeps the whole row: every probability is positive in exact arithmetic,
+  so no shorter prefix reaches 1 (a float64 cumulative sum can round to 1
+  early when a block's probability is below its resolution); likewise the
   whole row if rounding leaves the total mass below p.
 * R16 the scores are the float32 ones of R5/R6; the softmax and the
   cumulative sums here run in float64.  The GPU decides the prefix length in
@@ -68,8 +71,10 @@ def prefix_mass(s: np.ndarray, scale: float) -> Tuple[np.ndarray, np.ndarray]:
 
 def topp_count(s: np.ndarray, p: float, scale: float) -> int:
     """R15: the length of the shortest prefix with mass >= p (>= 1), or the
-    whole row when no prefix reaches p."""
+    whole row when p = 1 or no prefix reaches p."""
     _, F = prefix_mass(s, scale)
+    if float(p) >= 1.0:
+        return int(F.shape[0])
     hit = np.nonzero(F >= float(p))[0]
     return int(hit[0]) + 1 if hit.size else int(F.shape[0])
 

@@ -118,6 +118,9 @@ def test_limits():
     assert P.topp_row(s, float(prob.max()) * 0.5, 1.0).tolist() == [int(np.argmax(s))] == [17]
     # p = 1: every block (rounding may leave the total just below 1)
     assert P.topp_count(s, 1.0, 1.0) == 100
+    # p = 1 even where a probability underflows: exp(-1000) > 0 exactly
+    assert P.topp_row(np.array([0.0, -1000.0, 3.0], np.float32), 1.0, 1.0).tolist() == [0, 1, 2]
+    assert P.topp_row(np.array([0.0, -1000.0, 3.0], np.float32), 0.99, 1.0).tolist() == [0, 2]
     # a huge scale concentrates all the mass on the tied maxima
     assert P.topp_row(s, 0.4, 1e6).tolist() == [17]
     assert P.topp_row(s, 0.9, 1e6).tolist() == [17, 60]
