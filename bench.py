@@ -119,6 +119,55 @@ def cpu_baseline(inp, w, row_ptr, col_idx, sizes, step_flops, budget_s=20.0):
             "seconds_per_step": t_step}
 
 
+def time_select(vsa, lib, _lib, q, k, v, o, w, mode, val, sink, stream, sizes, reps=20):
+    """Mean plan time of vsa_plan_select for one selection, and attention
+    over the index it produces (both timed with events on the stream)."""
+    import ctypes
+
+    import torch
+    shape = vsa._shape_of(q, w.grid, w.block)
+    rl, cap, pws = vsa.query_select(shape, mode, [val], w.window_t, sink)
+    dev = q.device
+    row_ptr = torch.empty(rl, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(pws, 1), dtype=torch.uint8, device=dev)
+    cidx = _lib.VsaIndex(shape, 0, 0, ctypes.c_void_p(row_ptr.data_ptr()), ctypes.c_void_p(col_idx.data_ptr()), cap)
+    sel, _vals = vsa._select(shape, mode, [val], w.window_t, sink, None)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    qp, kp, vp, op = (ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, o))
+
+    def plan_call():
+        _lib.check(lib.vsa_plan_select(qp, kp, ctypes.byref(shape), ctypes.byref(sel), ctypes.byref(cidx),
+                                       ctypes.c_void_p(ws.data_ptr()), ws.numel(), sp), "vsa_plan_select")
+
+    def attn_call():
+        _lib.check(lib.vsa_attn(qp, kp, vp, ctypes.byref(cidx), ctypes.c_float(0.0), op, None, 0, sp), "vsa_attn")
+
+    for _ in range(2):
+        plan_call(); attn_call()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record(stream)
+    for _ in range(reps):
+        plan_call()
+    e[1].record(stream)
+    for _ in range(reps // 2):
+        attn_call()
+    e[2].record(stream)
+    torch.cuda.synchronize()
+    plan_ms = e[0].elapsed_time(e[1]) / reps
+    attn_ms = e[1].elapsed_time(e[2]) / (reps // 2)
+    rp = row_ptr.cpu().numpy().astype(np.int64)
+    ci = col_idx.cpu().numpy().astype(np.int64)[: int(rp[-1])]
+    flops = executed_flops(rp, ci, sizes, w.D)
+    lens = np.diff(rp)
+    return {"mode": mode, "value": val, "sink": sink, "window_t": w.window_t,
+            "plan_ms": round(plan_ms, 4), "attn_ms": round(attn_ms, 4),
+            "attn_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 2),
+            "nnz_blocks": int(rp[-1]), "density": round(float(rp[-1]) / (len(lens) * len(sizes)), 4),
+            "row_len_min_max": [int(lens.min()), int(lens.max())]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -275,6 +324,13 @@ def main():
             "algorithmic_bytes": sel_bytes, "GB_per_s": round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(sel_bytes / (sel_ms * 1e-3) / 8e12, 4),
             "choices": choice.cpu().tolist()}
+    # Selection variants (outside the timed step): Top-P and Top-K with
+    # attention-sink blocks, each planned in place into preallocated buffers
+    # and followed by attention over the index it produced.
+    if w.dtype == "bf16" and w.name == "wan13b":
+        result["select_variants"] = [
+            time_select(vsa, lib, _lib, q, k, v, o, w, mode, val, sink, stream, sizes)
+            for mode, val, sink in (("topp", 0.25, 2), ("topk", 0.2, 2))]
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inp, w, rp, ci, sizes, flops, a.cpu_budget)

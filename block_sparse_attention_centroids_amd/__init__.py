@@ -21,10 +21,10 @@ from typing import Optional, Sequence, Tuple, Union
 import torch
 
 from . import _lib
-from ._lib import VsaError, VsaIndex, VsaShape, check, load
+from ._lib import VsaError, VsaIndex, VsaSelect, VsaShape, check, load
 
-__all__ = ["plan", "attn", "query", "permute", "unpermute", "centroids", "centroid_scores",
-           "sics", "select_scheme", "Index", "VsaError", "load"]
+__all__ = ["plan", "plan_select", "attn", "query", "query_select", "permute", "unpermute",
+           "centroids", "centroid_scores", "sics", "select_scheme", "Index", "VsaError", "load"]
 
 _DTYPES = {torch.bfloat16: _lib.VSA_BF16, torch.float32: _lib.VSA_F32}
 
@@ -113,6 +113,53 @@ def plan(q: torch.Tensor, k: torch.Tensor, grid, block, density: Union[float, Se
     check(lib.vsa_plan(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
                        ctypes.byref(shape), dens, nd, int(window_t), ctypes.byref(cidx),
                        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(q)), "vsa_plan")
+    return Index(cidx.shape, cidx.nb, cidx.window_t, row_ptr, col_idx, cap)
+
+
+_MODES = {"topk": _lib.VSA_TOPK, "topp": _lib.VSA_TOPP}
+
+
+def _select(shape: VsaShape, mode: str, value, window_t: int, sink: int, scale: Optional[float]):
+    if mode not in _MODES:
+        raise ValueError(f"mode must be one of {sorted(_MODES)}")
+    vals, n = _densities(value, shape.heads)
+    sel = VsaSelect(_MODES[mode], n, ctypes.cast(vals, ctypes.POINTER(ctypes.c_float)), int(window_t),
+                    int(sink), 0.0 if scale is None else float(scale))
+    return sel, vals   # keep vals alive with sel
+
+
+def query_select(shape: VsaShape, mode: str, value, window_t: int = -1, sink: int = 0,
+                 scale: Optional[float] = None):
+    """(row_ptr_len, col_capacity, plan_ws_bytes) for plan_select."""
+    lib = load()
+    sel, _vals = _select(shape, mode, value, window_t, sink, scale)
+    rl, cap, pws = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
+    check(lib.vsa_query_select(ctypes.byref(shape), ctypes.byref(sel), ctypes.byref(rl),
+                               ctypes.byref(cap), ctypes.byref(pws)), "vsa_query_select")
+    return rl.value, cap.value, pws.value
+
+
+def plan_select(q: torch.Tensor, k: torch.Tensor, grid, block, mode: str,
+                value: Union[float, Sequence[float]], window_t: int = -1, sink: int = 0,
+                scale: Optional[float] = None) -> Index:
+    """Block means -> centroid scores -> per-row Top-K (value = keep rate)
+    or Top-P (value = cumulative threshold p of softmax(scale * scores)),
+    united with the temporal window and the first `sink` key blocks -> CSR."""
+    lib = load()
+    shape = _shape_of(q, grid, block)
+    if k.shape != q.shape or k.dtype != q.dtype or not k.is_contiguous():
+        raise ValueError("k must match q")
+    rl, cap, pws = query_select(shape, mode, value, window_t, sink, scale)
+    dev = q.device
+    row_ptr = torch.empty(rl, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(pws, 1), dtype=torch.uint8, device=dev)
+    cidx = VsaIndex(shape, 0, 0, ctypes.c_void_p(row_ptr.data_ptr()),
+                    ctypes.c_void_p(col_idx.data_ptr()), cap)
+    sel, _vals = _select(shape, mode, value, window_t, sink, scale)
+    check(lib.vsa_plan_select(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                              ctypes.byref(shape), ctypes.byref(sel), ctypes.byref(cidx),
+                              ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(q)), "vsa_plan_select")
     return Index(cidx.shape, cidx.nb, cidx.window_t, row_ptr, col_idx, cap)
 
 

@@ -18,6 +18,9 @@ VSA_ERR_HIP = 6
 VSA_BF16 = 0
 VSA_F32 = 1
 
+VSA_TOPK = 0
+VSA_TOPP = 1
+
 
 class VsaShape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("heads", ctypes.c_int32), ("D", ctypes.c_int32),
@@ -32,6 +35,12 @@ class VsaIndex(ctypes.Structure):
                 ("capacity", ctypes.c_int64)]
 
 
+class VsaSelect(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("n_value", ctypes.c_int32),
+                ("value", ctypes.POINTER(ctypes.c_float)), ("window_t", ctypes.c_int32),
+                ("sink", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
 class VsaError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -42,7 +51,7 @@ _lib = None
 
 EXPORTS = ("vsa_query", "vsa_plan", "vsa_attn", "vsa_permute", "vsa_unpermute",
            "vsa_centroids", "vsa_centroid_scores", "vsa_sics", "vsa_scheme_workspace",
-           "vsa_select_scheme", "vsa_status_str")
+           "vsa_select_scheme", "vsa_query_select", "vsa_plan_select", "vsa_status_str")
 
 
 def load() -> ctypes.CDLL:
@@ -73,6 +82,11 @@ def load() -> ctypes.CDLL:
                                          ctypes.POINTER(ctypes.c_size_t)]
     lib.vsa_select_scheme.argtypes = [P, P, ctypes.POINTER(VsaShape), ctypes.POINTER(ctypes.c_int32), I, P, P,
                                       P, ctypes.c_size_t, P]
+    lib.vsa_query_select.argtypes = [ctypes.POINTER(VsaShape), ctypes.POINTER(VsaSelect),
+                                     ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                                     ctypes.POINTER(ctypes.c_size_t)]
+    lib.vsa_plan_select.argtypes = [P, P, ctypes.POINTER(VsaShape), ctypes.POINTER(VsaSelect),
+                                    ctypes.POINTER(VsaIndex), P, ctypes.c_size_t, P]
     for name in EXPORTS[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     lib.vsa_status_str.argtypes = [ctypes.c_int]

@@ -74,13 +74,27 @@ vsa_status vsa_query(const vsa_shape* shape, const float* density, int n_density
   }
 }
 
-vsa_status vsa_plan(const void* q, const void* k, const vsa_shape* shape, const float* density,
-                    int n_density, int window_t, vsa_index* index, void* ws, size_t ws_bytes,
-                    void* stream) {
+vsa_status vsa_query_select(const vsa_shape* shape, const vsa_select* sel, int64_t* row_ptr_len,
+                            int64_t* col_capacity, size_t* plan_ws) {
+  try {
+    PlanSizes ps;
+    vsa_status st = select_sizes(shape, sel, &ps);
+    if (st != VSA_OK) return st;
+    if (row_ptr_len) *row_ptr_len = ps.rows + 1;
+    if (col_capacity) *col_capacity = ps.capacity;
+    if (plan_ws) *plan_ws = ps.ws;
+    return VSA_OK;
+  } catch (...) {
+    return VSA_ERR_INVALID_ARG;
+  }
+}
+
+vsa_status vsa_plan_select(const void* q, const void* k, const vsa_shape* shape, const vsa_select* sel,
+                           vsa_index* index, void* ws, size_t ws_bytes, void* stream) {
   try {
     if (!q || !k || !index || !ws) return VSA_ERR_INVALID_ARG;
     PlanSizes ps;
-    vsa_status st = plan_sizes(shape, density, n_density, window_t, &ps);
+    vsa_status st = select_sizes(shape, sel, &ps);
     if (st != VSA_OK) return st;
     if (!index->row_ptr || !index->col_idx) return VSA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(ws)) return VSA_ERR_INVALID_ARG;
@@ -96,34 +110,56 @@ vsa_status vsa_plan(const void* q, const void* k, const vsa_shape* shape, const 
 
     SelectArgs sa;
     std::memset(&sa, 0, sizeof(sa));
+    const bool topp = sel->mode == VSA_TOPP;
     int64_t sumk = 0;
     for (int h = 0; h < shape->heads; ++h) {
-      sa.k[h] = ps.k[h];
-      sa.off[h] = static_cast<int32_t>(sumk);
-      sumk += ps.k[h];
+      if (topp) {
+        sa.p[h] = ps.p[h];
+      } else {
+        sa.k[h] = ps.k[h];
+        sa.off[h] = static_cast<int32_t>(sumk);
+        sumk += ps.k[h];
+      }
     }
     sa.batch_stride = sumk * g.NB;
     sa.rows = ps.rows;
-    sa.window_t = window_t;
+    sa.window_t = sel->window_t;
     sa.words = ps.words;
-    int32_t* counts = window_t >= 0 ? reinterpret_cast<int32_t*>(w + ps.off_cnt) : nullptr;
-    uint64_t* bits = window_t >= 0 ? reinterpret_cast<uint64_t*>(w + ps.off_bits) : nullptr;
+    sa.sink = sel->sink;
+    sa.bitmap = ps.bitmap ? 1 : 0;
+    sa.scale = ps.scale;
+    sa.topp = topp ? 1 : 0;
+    int32_t* counts = ps.bitmap ? reinterpret_cast<int32_t*>(w + ps.off_cnt) : nullptr;
+    uint64_t* bits = ps.bitmap ? reinterpret_cast<uint64_t*>(w + ps.off_bits) : nullptr;
 
     index->shape = *shape;
     index->nb = g.NB;
-    index->window_t = window_t;
+    index->window_t = sel->window_t;
 
     hipError_t e = launch_pool(q, qc, k, kc, shape->dtype, shape->D, dg, BH, st_);
     if (e == hipSuccess)
       e = launch_score_select(qc, kc, dg, shape->D, shape->heads, BH, sa, index->row_ptr,
                               index->col_idx, counts, bits, st_);
-    if (e == hipSuccess && window_t >= 0)
+    if (e == hipSuccess && ps.bitmap)
       e = launch_scan_fill(counts, bits, index->row_ptr, index->col_idx, ps.rows, ps.words, g.NB,
                            index->capacity, st_);
     return hip_status(e);
   } catch (...) {
     return VSA_ERR_INVALID_ARG;
   }
+}
+
+vsa_status vsa_plan(const void* q, const void* k, const vsa_shape* shape, const float* density,
+                    int n_density, int window_t, vsa_index* index, void* ws, size_t ws_bytes,
+                    void* stream) {
+  vsa_select sel;
+  sel.mode = VSA_TOPK;
+  sel.n_value = n_density;
+  sel.value = density;
+  sel.window_t = window_t;
+  sel.sink = 0;
+  sel.scale = 0.0f;
+  return vsa_plan_select(q, k, shape, &sel, index, ws, ws_bytes, stream);
 }
 
 vsa_status vsa_attn(const void* q, const void* k, const void* v, const vsa_index* index,

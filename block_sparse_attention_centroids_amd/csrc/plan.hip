@@ -1,13 +1,16 @@
 // Planning kernels for gfx950: block means (the summarizer), centroid dot
-// products (the inter-estimator) with per-row top-k selection and the local
-// temporal window, and the CSR scan/fill used when rows vary in length.
-// SPADE (arXiv 2608.03335) 3.1 Fig. 4(c) and 3.3.
+// products (the inter-estimator) with per-row Top-K or Top-P selection
+// united with the local temporal window and the attention-sink blocks, and
+// the CSR scan/fill used when rows vary in length.  SPADE (arXiv
+// 2608.03335) 3.1 Fig. 4(c) and the vDiT-SSR utility parameters, and 3.3.
 //
 // This file is built with -ffp-contract=off and every product/sum uses the
 // explicitly rounded intrinsics, so the arithmetic is the fixed float32
 // order that makes the index reproducible bit for bit:
 //   mean  = (((+0 + x_0) + x_1) + ... + x_{n-1}) / n
 //   score = ((+0 + q_0*k_0) + q_1*k_1) + ... + q_{D-1}*k_{D-1}
+// Top-P weights are expf((score - row max) * scale), summed in one fixed
+// order per row (see topp_cut_regs).
 #include <hip/hip_runtime.h>
 
 #include "vsa_device.h"
@@ -133,14 +136,197 @@ __device__ inline uint32_t order_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Float of an order key (the inverse of order_key; -0 arrives as +0).
+__device__ inline float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Same value in every lane, taken from lane 0 (keeps decisions uniform).
+__device__ inline float uniform_f(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+// Sum over the wave: each lane's partial, then a butterfly.  The pairs of a
+// butterfly step add the same two numbers, so every lane ends with the same
+// value.
+__device__ inline float wave_sum_f(float a) {
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) a = __fadd_rn(a, __shfl_xor(a, m, 64));
+  return uniform_f(a);
+}
+
+__device__ inline uint32_t wave_max_u(uint32_t v) {
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, m, 64));
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+
+// Top-K cut of a row of keys: thr = the k-th largest key, need = how many
+// keys equal to thr are kept (the lowest ids).  thr grows bit by bit from
+// the top to the largest value with at least kk keys >= thr; counts are
+// ballots, and rows of at most 512 blocks keep their keys in registers.
+__device__ inline void topk_cut(const uint32_t* keys, int NB, int lane, int kk, uint32_t& thr_out,
+                                int& need_out) {
+  uint32_t thr = 0u;
+  int gt = 0;
+  if (NB <= 64 * 8) {
+    uint32_t kv[8];
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) {
+      const int j = s2 * 64 + lane;
+      kv[s2] = j < NB ? keys[j] : 0u;   // below every real key
+    }
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = thr | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) cnt += __popcll(__ballot(kv[s2] >= cand));
+      if (cnt >= kk) thr = cand;
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) gt += __popcll(__ballot(kv[s2] > thr));
+  } else {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = thr | (1u << bit);
+      int cnt = 0;
+      for (int j0 = 0; j0 < NB; j0 += 64) {
+        const int j = j0 + lane;
+        cnt += __popcll(__ballot(j < NB && keys[j] >= cand));
+      }
+      if (cnt >= kk) thr = cand;
+    }
+    for (int j0 = 0; j0 < NB; j0 += 64) {
+      const int j = j0 + lane;
+      gt += __popcll(__ballot(j < NB && keys[j] > thr));
+    }
+  }
+  thr_out = thr;
+  need_out = kk - gt;   // >= 1
+}
+
+// Top-P cut of a row of keys.  Weights e_j = expf((s_j - m) * scale) with m
+// the row max; M(t) = sum of the weights of keys >= t, always summed the
+// same way (per lane in chunk order, then the butterfly), so M is
+// non-increasing in t and M(0) is the total Z.  With T = p * Z (<= Z for
+// p <= 1), thr is the largest key with M(thr) >= T, found bit by bit; every
+// key above thr is kept, and keys equal to thr are added in id order until
+// the running mass reaches T (at least one of them).  p = 1 keeps the
+// whole row: every weight is positive in exact arithmetic, even one too
+// small to change a float32 sum.
+template <int NR>
+__device__ inline void topp_cut_regs(const uint32_t* keys, int NB, int lane, float p, float scale,
+                                     uint32_t& thr_out, int& need_out) {
+  if (p >= 1.0f) {
+    thr_out = 0u;
+    need_out = NB;
+    return;
+  }
+  uint32_t kv[NR];
+  float ev[NR];
+  uint32_t kmax = 0u;
+#pragma unroll
+  for (int s2 = 0; s2 < NR; ++s2) {
+    const int j = s2 * 64 + lane;
+    kv[s2] = j < NB ? keys[j] : 0u;
+    kmax = max(kmax, kv[s2]);
+  }
+  const float smax = key_float(wave_max_u(kmax));
+#pragma unroll
+  for (int s2 = 0; s2 < NR; ++s2) {
+    const int j = s2 * 64 + lane;
+    ev[s2] = j < NB ? expf(__fmul_rn(__fsub_rn(key_float(kv[s2]), smax), scale)) : 0.0f;
+  }
+  auto mass_ge = [&](uint32_t t) {
+    float a = 0.0f;
+#pragma unroll
+    for (int s2 = 0; s2 < NR; ++s2) a = __fadd_rn(a, kv[s2] >= t ? ev[s2] : 0.0f);
+    return wave_sum_f(a);
+  };
+  const float target = __fmul_rn(p, mass_ge(0u));
+  uint32_t thr = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    if (mass_ge(cand) >= target) thr = cand;
+  }
+  float acc = 0.0f;
+  int neq = 0;
+  {
+    float a = 0.0f;
+#pragma unroll
+    for (int s2 = 0; s2 < NR; ++s2) {
+      const int j = s2 * 64 + lane;
+      a = __fadd_rn(a, kv[s2] > thr ? ev[s2] : 0.0f);
+      neq += __popcll(__ballot(j < NB && kv[s2] == thr));
+    }
+    acc = wave_sum_f(a);
+  }
+  const float ethr = expf(__fmul_rn(__fsub_rn(key_float(thr), smax), scale));
+  int need = 0;
+  while (need < neq && acc < target) {
+    acc = __fadd_rn(acc, ethr);
+    ++need;
+  }
+  thr_out = thr;
+  need_out = need > 0 ? need : 1;
+}
+
+// The same cut for rows longer than the register chunks: keys stay in LDS
+// and each weight is recomputed when it is needed (the same expression, so
+// the same value).
+__device__ inline void topp_cut_lds(const uint32_t* keys, int NB, int lane, float p, float scale,
+                                    uint32_t& thr_out, int& need_out) {
+  if (p >= 1.0f) {
+    thr_out = 0u;
+    need_out = NB;
+    return;
+  }
+  uint32_t kmax = 0u;
+  for (int j = lane; j < NB; j += 64) kmax = max(kmax, keys[j]);
+  const float smax = key_float(wave_max_u(kmax));
+  auto weight = [&](uint32_t key) { return expf(__fmul_rn(__fsub_rn(key_float(key), smax), scale)); };
+  auto mass_ge = [&](uint32_t t) {
+    float a = 0.0f;
+    for (int j0 = 0; j0 < NB; j0 += 64) {
+      const int j = j0 + lane;
+      const uint32_t key = j < NB ? keys[j] : 0u;
+      a = __fadd_rn(a, (j < NB && key >= t) ? weight(key) : 0.0f);
+    }
+    return wave_sum_f(a);
+  };
+  const float target = __fmul_rn(p, mass_ge(0u));
+  uint32_t thr = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    if (mass_ge(cand) >= target) thr = cand;
+  }
+  float a = 0.0f;
+  int neq = 0;
+  for (int j0 = 0; j0 < NB; j0 += 64) {
+    const int j = j0 + lane;
+    const uint32_t key = j < NB ? keys[j] : 0u;
+    a = __fadd_rn(a, (j < NB && key > thr) ? weight(key) : 0.0f);
+    neq += __popcll(__ballot(j < NB && key == thr));
+  }
+  float acc = wave_sum_f(a);
+  const float ethr = weight(thr);
+  int need = 0;
+  while (need < neq && acc < target) {
+    acc = __fadd_rn(acc, ethr);
+    ++need;
+  }
+  thr_out = thr;
+  need_out = need > 0 ? need : 1;
+}
+
 // ---------------------------------------------------------------------------
 // Scores + selection.  One workgroup per (bh, tile of RT query blocks).
 // Phase 1 fills LDS with the RT x NB score rows; phase 2 gives each wave a
-// row: the k-th largest key is found bit by bit from the top (a count of
-// keys >= candidate per bit), then the row is emitted in ascending block id
-// with ties at the threshold going to the lowest ids.
+// row: the cut (Top-K or Top-P) gives a threshold key and how many keys
+// equal to it are kept, then the row is emitted in ascending block id with
+// ties at the threshold going to the lowest ids, united with the window and
+// the sink blocks.
 // ---------------------------------------------------------------------------
-template <int RT>
+template <int RT, bool TOPP>
 __global__ __launch_bounds__(256) void score_select_kernel(
     const float* __restrict__ qc, const float* __restrict__ kc, DGeo g, int D, int heads,
     SelectArgs sa, int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
@@ -174,51 +360,24 @@ __global__ __launch_bounds__(256) void score_select_kernel(
   // Phase 2: selection, one wave per row.
   const int h = bh % heads;
   const int b = bh / heads;
-  const int kk = sa.k[h];
+  const int kk = TOPP ? 0 : sa.k[h];
   const int per_t = g.nbh * g.nbw;
   for (int r = wave; r < rows_here; r += 4) {
     const int i = i0 + r;
     const uint32_t* keys = smem + r * NB;
-    // k-th largest key, bit by bit from the top: thr grows to the largest
-    // value with at least kk keys >= thr.  Counts are ballots; rows of at
-    // most 512 blocks keep their keys in registers.
-    uint32_t thr = 0u;
-    int gt = 0;
-    if (NB <= 64 * 8) {
-      uint32_t kv[8];
-#pragma unroll
-      for (int s2 = 0; s2 < 8; ++s2) {
-        const int j = s2 * 64 + lane;
-        kv[s2] = j < NB ? keys[j] : 0u;   // below every real key
-      }
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = thr | (1u << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int s2 = 0; s2 < 8; ++s2) cnt += __popcll(__ballot(kv[s2] >= cand));
-        if (cnt >= kk) thr = cand;
-      }
-#pragma unroll
-      for (int s2 = 0; s2 < 8; ++s2) gt += __popcll(__ballot(kv[s2] > thr));
+    uint32_t thr;
+    int need;
+    if constexpr (TOPP) {
+      if (NB <= 64 * 8)
+        topp_cut_regs<8>(keys, NB, lane, sa.p[h], sa.scale, thr, need);
+      else
+        topp_cut_lds(keys, NB, lane, sa.p[h], sa.scale, thr, need);
     } else {
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = thr | (1u << bit);
-        int cnt = 0;
-        for (int j0 = 0; j0 < NB; j0 += 64) {
-          const int j = j0 + lane;
-          cnt += __popcll(__ballot(j < NB && keys[j] >= cand));
-        }
-        if (cnt >= kk) thr = cand;
-      }
-      for (int j0 = 0; j0 < NB; j0 += 64) {
-        const int j = j0 + lane;
-        gt += __popcll(__ballot(j < NB && keys[j] > thr));
-      }
+      topk_cut(keys, NB, lane, kk, thr, need);
     }
-    const int need = kk - gt;   // >= 1 keys equal to thr are kept, lowest ids first
     const int tbi = i / per_t;
     const int64_t row = (int64_t)bh * NB + i;
-    const int64_t out0 = (int64_t)b * sa.batch_stride + (int64_t)NB * sa.off[h] + (int64_t)i * kk;
+    const int64_t out0 = TOPP ? 0 : (int64_t)b * sa.batch_stride + (int64_t)NB * sa.off[h] + (int64_t)i * kk;
     int eq_before = 0, base = 0;
     const uint64_t lt = lanemask_lt();
     for (int s = 0; s * 64 < NB; ++s) {
@@ -229,12 +388,12 @@ __global__ __launch_bounds__(256) void score_select_kernel(
       const uint64_t eqm = __ballot(eq);
       const int rank_eq = eq_before + __popcll(eqm & lt);
       bool keep = valid && (key > thr || (eq && rank_eq < need));
-      if (sa.window_t >= 0 && valid) {
+      if (sa.bitmap && valid) {
         const int dt = j / per_t - tbi;
-        keep = keep || (dt <= sa.window_t && -dt <= sa.window_t);
+        keep = keep || (sa.window_t >= 0 && dt <= sa.window_t && -dt <= sa.window_t) || j < sa.sink;
       }
       const uint64_t km = __ballot(keep);
-      if (sa.window_t >= 0) {
+      if (sa.bitmap) {
         if (lane == 0) bits[row * sa.words + s] = km;
       } else if (keep) {
         const int pos = base + __popcll(km & lt);
@@ -244,7 +403,7 @@ __global__ __launch_bounds__(256) void score_select_kernel(
       eq_before += __popcll(eqm);
     }
     if (lane == 0) {
-      if (sa.window_t >= 0) {
+      if (sa.bitmap) {
         counts[row] = base;
       } else {
         row_ptr[row] = (int32_t)out0;
@@ -344,18 +503,28 @@ int select_rows_per_block(int NB) {
   return 1;
 }
 
+template <bool TOPP>
+void launch_score_select_t(int RT, dim3 grid, dim3 block, size_t lds, hipStream_t st, const float* qc,
+                           const float* kc, const DGeo& g, int D, int heads, const SelectArgs& sa,
+                           int32_t* row_ptr, int32_t* col_idx, int32_t* counts, uint64_t* bits) {
+  switch (RT) {
+    case 8: hipLaunchKernelGGL((score_select_kernel<8, TOPP>), grid, block, lds, st, qc, kc, g, D, heads, sa, row_ptr, col_idx, counts, bits); break;
+    case 4: hipLaunchKernelGGL((score_select_kernel<4, TOPP>), grid, block, lds, st, qc, kc, g, D, heads, sa, row_ptr, col_idx, counts, bits); break;
+    case 2: hipLaunchKernelGGL((score_select_kernel<2, TOPP>), grid, block, lds, st, qc, kc, g, D, heads, sa, row_ptr, col_idx, counts, bits); break;
+    default: hipLaunchKernelGGL((score_select_kernel<1, TOPP>), grid, block, lds, st, qc, kc, g, D, heads, sa, row_ptr, col_idx, counts, bits); break;
+  }
+}
+
 hipError_t launch_score_select(const float* qc, const float* kc, const DGeo& g, int D, int heads,
                                int BH, const SelectArgs& sa, int32_t* row_ptr, int32_t* col_idx,
                                int32_t* counts, uint64_t* bits, hipStream_t st) {
   const int RT = select_rows_per_block(g.NB);
   dim3 grid((g.NB + RT - 1) / RT, BH), block(256);
   size_t lds = (size_t)RT * g.NB * sizeof(uint32_t);
-  switch (RT) {
-    case 8: hipLaunchKernelGGL(score_select_kernel<8>, grid, block, lds, st, qc, kc, g, D, heads, sa, row_ptr, col_idx, counts, bits); break;
-    case 4: hipLaunchKernelGGL(score_select_kernel<4>, grid, block, lds, st, qc, kc, g, D, heads, sa, row_ptr, col_idx, counts, bits); break;
-    case 2: hipLaunchKernelGGL(score_select_kernel<2>, grid, block, lds, st, qc, kc, g, D, heads, sa, row_ptr, col_idx, counts, bits); break;
-    default: hipLaunchKernelGGL(score_select_kernel<1>, grid, block, lds, st, qc, kc, g, D, heads, sa, row_ptr, col_idx, counts, bits); break;
-  }
+  if (sa.topp)
+    launch_score_select_t<true>(RT, grid, block, lds, st, qc, kc, g, D, heads, sa, row_ptr, col_idx, counts, bits);
+  else
+    launch_score_select_t<false>(RT, grid, block, lds, st, qc, kc, g, D, heads, sa, row_ptr, col_idx, counts, bits);
   return hipGetLastError();
 }
 

@@ -91,40 +91,57 @@ inline vsa_status check_shape(const vsa_shape* s) {
 
 struct PlanSizes {
   int64_t rows = 0;          // B*heads*NB
-  int64_t capacity = 0;      // col_idx entries needed (upper bound with a window)
+  int64_t capacity = 0;      // col_idx entries needed (an upper bound in bitmap mode)
   size_t ws = 0;             // plan workspace bytes
   size_t off_qc = 0, off_kc = 0, off_cnt = 0, off_bits = 0;
-  int words = 0;             // 64-bit bitmap words per row (window mode)
-  std::vector<int> k;        // per head
+  int words = 0;             // 64-bit bitmap words per row
+  bool bitmap = false;       // rows vary in length: bitmap + scan + fill
+  float scale = 0.0f;        // Top-P logit scale (resolved)
+  std::vector<int> k;        // per head (Top-K)
+  std::vector<float> p;      // per head (Top-P)
 };
 
-inline vsa_status plan_sizes(const vsa_shape* s, const float* density, int n_density,
-                             int window_t, PlanSizes* out) {
+// Sizes and per-head parameters of a selection; validates everything the
+// host can see.
+inline vsa_status select_sizes(const vsa_shape* s, const vsa_select* sel, PlanSizes* out) {
   vsa_status st = check_shape(s);
   if (st != VSA_OK) return st;
-  if (!density || !out) return VSA_ERR_INVALID_ARG;
-  if (n_density != 1 && n_density != s->heads) return VSA_ERR_INVALID_ARG;
-  if (window_t < -1) return VSA_ERR_INVALID_ARG;
+  if (!sel || !sel->value || !out) return VSA_ERR_INVALID_ARG;
+  if (sel->mode != VSA_TOPK && sel->mode != VSA_TOPP) return VSA_ERR_INVALID_ARG;
+  if (sel->n_value != 1 && sel->n_value != s->heads) return VSA_ERR_INVALID_ARG;
+  if (sel->window_t < -1) return VSA_ERR_INVALID_ARG;
   if (s->heads > VSA_MAX_HEADS) return VSA_ERR_UNSUPPORTED;
   Geo g = make_geo(*s);
+  if (sel->sink < 0 || sel->sink > g.NB) return VSA_ERR_INVALID_ARG;
+  if (!(sel->scale >= 0.0f) || !std::isfinite(sel->scale)) return VSA_ERR_INVALID_ARG;
+  const bool topp = sel->mode == VSA_TOPP;
   out->k.assign(s->heads, 0);
+  out->p.assign(s->heads, 0.0f);
   for (int h = 0; h < s->heads; ++h) {
-    float d = density[n_density == 1 ? 0 : h];
+    float d = sel->value[sel->n_value == 1 ? 0 : h];
     if (!(d > 0.0f) || !(d <= 1.0f)) return VSA_ERR_INVALID_ARG;  // also rejects NaN
-    out->k[h] = k_rule(d, g.NB);
+    if (topp)
+      out->p[h] = d;
+    else
+      out->k[h] = k_rule(d, g.NB);
   }
+  out->scale = sel->scale != 0.0f ? sel->scale : 1.0f / std::sqrt(static_cast<float>(s->D));
   out->rows = int64_t(s->B) * s->heads * g.NB;
   int64_t cap = 0;
-  for (int h = 0; h < s->heads; ++h) {
-    int64_t per_head = 0;
-    for (int i = 0; i < g.NB; ++i) {
-      int tb = i / (g.nbh * g.nbw);
-      int64_t c = out->k[h] + window_count(g, tb, window_t);
-      per_head += std::min<int64_t>(c, g.NB);
+  if (topp) {
+    cap = out->rows * g.NB;
+  } else {
+    for (int h = 0; h < s->heads; ++h) {
+      int64_t per_head = 0;
+      for (int i = 0; i < g.NB; ++i) {
+        int tb = i / (g.nbh * g.nbw);
+        int64_t c = int64_t(out->k[h]) + window_count(g, tb, sel->window_t) + sel->sink;
+        per_head += std::min<int64_t>(c, g.NB);
+      }
+      cap += per_head;
     }
-    cap += per_head;
+    cap *= s->B;
   }
-  cap *= s->B;
   if (cap >= (int64_t(1) << 31) - 1) return VSA_ERR_UNSUPPORTED;
   out->capacity = cap;
   size_t cent = size_t(out->rows) * s->D * sizeof(float);
@@ -132,7 +149,8 @@ inline vsa_status plan_sizes(const vsa_shape* s, const float* density, int n_den
   out->off_kc = align256(cent);
   size_t ws = out->off_kc + align256(cent);
   out->words = (g.NB + 63) / 64;
-  if (window_t >= 0) {
+  out->bitmap = topp || sel->window_t >= 0 || sel->sink > 0;
+  if (out->bitmap) {
     out->off_cnt = ws;
     ws += align256(size_t(out->rows + 1) * sizeof(int32_t));
     out->off_bits = ws;
@@ -140,6 +158,19 @@ inline vsa_status plan_sizes(const vsa_shape* s, const float* density, int n_den
   }
   out->ws = ws;
   return VSA_OK;
+}
+
+// Top-K with an optional window: the selection of vsa_query / vsa_plan.
+inline vsa_status plan_sizes(const vsa_shape* s, const float* density, int n_density,
+                             int window_t, PlanSizes* out) {
+  vsa_select sel;
+  sel.mode = VSA_TOPK;
+  sel.n_value = n_density;
+  sel.value = density;
+  sel.window_t = window_t;
+  sel.sink = 0;
+  sel.scale = 0.0f;
+  return select_sizes(s, &sel, out);
 }
 
 }  // namespace vsa

@@ -11,12 +11,19 @@ namespace vsa {
 
 // Per-head selection parameters, passed by value as a kernel argument.
 struct SelectArgs {
-  int32_t k[VSA_MAX_HEADS];     // kept blocks per query-block row of head h
-  int32_t off[VSA_MAX_HEADS];   // sum of k over heads before h
-  int64_t batch_stride;         // NB * sum_h k_h: col_idx entries per batch item
+  union {
+    int32_t k[VSA_MAX_HEADS];   // Top-K: kept blocks per query-block row of head h
+    float p[VSA_MAX_HEADS];     // Top-P: cumulative threshold of head h
+  };
+  int32_t off[VSA_MAX_HEADS];   // Top-K: sum of k over heads before h
+  int64_t batch_stride;         // Top-K: NB * sum_h k_h, col_idx entries per batch item
   int64_t rows;                 // B * heads * NB
   int32_t window_t;             // -1: none
   int32_t words;                // 64-bit bitmap words per row
+  int32_t sink;                 // key blocks 0 .. sink-1 kept by every row
+  int32_t bitmap;               // rows vary: write bitmaps and counts for scan + fill
+  float scale;                  // Top-P logit scale
+  int32_t topp;                 // selection mode: 0 Top-K, 1 Top-P
 };
 
 // Per-candidate layout of the block SICS in the scheme workspace: candidate

@@ -101,6 +101,35 @@ vsa_status vsa_query(const vsa_shape* shape, const float* density, int n_density
                      int window_t, int64_t* row_ptr_len, int64_t* col_capacity,
                      size_t* plan_ws, size_t* attn_ws);
 
+/* Selection mode of vsa_plan_select (SPADE 3.1: the Top-K / Top-P mode of a
+ * head's scheme). */
+typedef enum { VSA_TOPK = 0, VSA_TOPP = 1 } vsa_select_mode;
+
+/* Selection options of vsa_query_select / vsa_plan_select (SPADE 3.1:
+ * each head's scheme has a local-window length and an inter-top value that
+ * is a Top-K keep or a Top-P cumulative threshold; the attention-sink
+ * length is a utility parameter; 3.3: the filtered scores are united with
+ * the window and sink masks).
+ * mode: vsa_select_mode.
+ * value: host float[n_value], n_value = 1 (all heads) or heads, each in
+ *   (0, 1]: the keep rate for VSA_TOPK (k as in vsa_query), the threshold p
+ *   for VSA_TOPP: a query-block row keeps the shortest prefix of its key
+ *   blocks, ordered by score descending and block id ascending, whose
+ *   softmax(scale * scores) mass is at least p (at least one block; p = 1
+ *   keeps the whole row).
+ * window_t: as in vsa_query.
+ * sink: 0 <= sink <= NB; key blocks 0 .. sink-1 are kept by every row.
+ * scale: VSA_TOPP logit scale, 0 means 1/sqrt(D); must be finite and
+ *   non-negative. */
+typedef struct {
+  int32_t mode;
+  int32_t n_value;
+  const float* value;
+  int32_t window_t;
+  int32_t sink;
+  float scale;
+} vsa_select;
+
 /* Planning (SPADE 3.3: summarizer, inter-estimator, Top-K, union with the
  * local window).  q, k: device [B, heads, N, D] of shape->dtype.  Block
  * means and their dot products are computed in float32 in a fixed order:
@@ -112,6 +141,26 @@ vsa_status vsa_query(const vsa_shape* shape, const float* density, int n_density
 vsa_status vsa_plan(const void* q, const void* k, const vsa_shape* shape,
                     const float* density, int n_density, int window_t,
                     vsa_index* index, void* ws, size_t ws_bytes, void* stream);
+
+/* Host-only sizing for vsa_plan_select; touches no device.  Outputs as in
+ * vsa_query.  col_capacity is exact for VSA_TOPK without window and sink,
+ * min(NB, k + window + sink) per row with them, and NB per row for
+ * VSA_TOPP (any prefix length is possible). */
+vsa_status vsa_query_select(const vsa_shape* shape, const vsa_select* sel, int64_t* row_ptr_len,
+                            int64_t* col_capacity, size_t* plan_ws);
+
+/* Planning with a selection mode and sink blocks (SPADE 3.1 and 3.3).
+ * Same inputs, arithmetic and CSR output as vsa_plan, which equals
+ * vsa_plan_select with VSA_TOPK, the density as value and sink 0.
+ * VSA_TOPP works in float32 on the scores of the fixed order above: the
+ * row max m, weights e_j = expf((s_j - m) * scale), sums over a wave in a
+ * fixed order, and the prefix cut found by a search on the score keys,
+ * so the index is reproducible; ties at the cut keep the lower ids.
+ * Scores are assumed finite.  index->capacity must be at least
+ * vsa_query_select's col_capacity; ws at least its plan_ws bytes. */
+vsa_status vsa_plan_select(const void* q, const void* k, const vsa_shape* shape,
+                           const vsa_select* sel, vsa_index* index, void* ws, size_t ws_bytes,
+                           void* stream);
 
 /* Block-sparse attention (SPADE 2.2 Eq. 2 with M = 0 on kept block pairs and
  * -inf elsewhere; 3.3 flash block-sparse attention and layout restore).

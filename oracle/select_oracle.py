@@ -17,7 +17,7 @@ Diffusion Models Inference" (arXiv 2608.03335):
 
 Readings where the pages are silent (also listed in the design notes):
 
-* R15 Top-P normalizes a query-block row with a softmax of its centroid
+* R21 Top-P normalizes a query-block row with a softmax of its centroid
   scores times the logit scale (1/sqrt(d) unless given):
   prob_j = exp(scale*s_j) / sum_l exp(scale*s_l).  It keeps the shortest
   prefix of the row, taken in (score descending, block id ascending) order,
@@ -26,14 +26,14 @@ Readings where the pages are silent (also listed in the design notes):
   so no shorter prefix reaches 1 (a float64 cumulative sum can round to 1
   early when a block's probability is below its resolution); likewise the
   whole row if rounding leaves the total mass below p.
-* R16 the scores are the float32 ones of R5/R6; the softmax and the
+* R22 the scores are the float32 ones of R5/R6; the softmax and the
   cumulative sums here run in float64.  The GPU decides the prefix length in
   float32: where a prefix's float64 mass lies within the float32 error bound
   of p, either side of it is accepted by the tests.
-* R17 an attention-sink length s counts key blocks: blocks 0 .. s-1 (the
+* R23 an attention-sink length s counts key blocks: blocks 0 .. s-1 (the
   first blocks of the blocked key sequence, i.e. the first temporal slab's
   leading blocks) are kept by every query-block row; s = 0 means none.
-* R18 the kept set of a row is the union of its Top-K or Top-P selection,
+* R24 the kept set of a row is the union of its Top-K or Top-P selection,
   its local window (R8) and the sink blocks, listed in ascending id (R9).
 """
 from __future__ import annotations
@@ -55,7 +55,7 @@ def rank_order(s: np.ndarray) -> np.ndarray:
 
 
 def row_probabilities(s: np.ndarray, scale: float) -> np.ndarray:
-    """R15: softmax of scale * s over the row, in float64 (max subtracted
+    """R21: softmax of scale * s over the row, in float64 (max subtracted
     first, which leaves the quotient unchanged)."""
     z = np.asarray(s, dtype=np.float32).astype(np.float64) * float(scale)
     e = np.exp(z - z.max())
@@ -70,7 +70,7 @@ def prefix_mass(s: np.ndarray, scale: float) -> Tuple[np.ndarray, np.ndarray]:
 
 
 def topp_count(s: np.ndarray, p: float, scale: float) -> int:
-    """R15: the length of the shortest prefix with mass >= p (>= 1), or the
+    """R21: the length of the shortest prefix with mass >= p (>= 1), or the
     whole row when p = 1 or no prefix reaches p."""
     _, F = prefix_mass(s, scale)
     if float(p) >= 1.0:
@@ -86,7 +86,7 @@ def topp_row(s: np.ndarray, p: float, scale: float) -> np.ndarray:
 
 
 def sink_blocks(NB: int, sink: int) -> np.ndarray:
-    """R17: the first `sink` key blocks."""
+    """R23: the first `sink` key blocks."""
     return np.arange(min(int(sink), int(NB)), dtype=np.int64)
 
 
@@ -96,7 +96,7 @@ def select_rows(S: np.ndarray, mode: str, values: Sequence[float], g: "O.Geometr
 
     mode "topk": values are per-head keep rates (k by R4); mode "topp":
     values are per-head cumulative thresholds p.  Every row is united with
-    the window (R8) and the sink blocks (R17).  Returns (row_ptr, col_idx)
+    the window (R8) and the sink blocks (R23).  Returns (row_ptr, col_idx)
     in the CSR layout of R9."""
     B, Hh, NB, _ = S.shape
     vals = np.broadcast_to(np.asarray(values, dtype=np.float32), (Hh,))

@@ -16,14 +16,14 @@ blocking scheme is the candidate with the highest aggregation score.
 
 Readings where the pages are silent (also listed in the design notes):
 
-* R11 ragged edges: a cut-short block's SICS runs over its valid tokens
+* R17 ragged edges: a cut-short block's SICS runs over its valid tokens
   (BS = that block's token count).
-* R12 a zero token vector normalizes to the zero vector: its cosine
+* R18 a zero token vector normalizes to the zero vector: its cosine
   similarity with anything, itself included, is 0, so the diagonal term BS
   of Algorithm 1 counts the nonzero tokens only.
-* R13 a head's scheme score is AS(Q | scheme) + AS(K | scheme) (the module
+* R19 a head's scheme score is AS(Q | scheme) + AS(K | scheme) (the module
   aggregates "Q and K under each" candidate).
-* R14 the selected scheme is the first candidate (lowest index) with the
+* R20 the selected scheme is the first candidate (lowest index) with the
   highest score.  The GPU decides in float32; where two candidates' float64
   scores lie within the float32 error bound of each other, either choice
   is accepted by the tests.
@@ -47,7 +47,7 @@ def sics_online(xb: np.ndarray) -> float:
     nonzero = 0
     for x in xb:
         norm = float(np.sqrt(np.dot(x, x)))
-        if norm == 0.0:      # R12
+        if norm == 0.0:      # R18
             continue
         xh = x / norm
         sigma += float(np.dot(r, xh))
@@ -78,7 +78,7 @@ def _sics_online_many(xb: np.ndarray) -> np.ndarray:
 def block_sics(x: np.ndarray, g: "O.Geometry", heads: Sequence[int] = None) -> np.ndarray:
     """SICS of every block of x [B, heads, N, d] under the blocking of g:
     float64 [B, heads, NB], each block by Algorithm 1 over its tokens in
-    block order (R11).  heads limits the work to some heads (the others
+    block order (R17).  heads limits the work to some heads (the others
     stay zero)."""
     B, Hh = x.shape[:2]
     out = np.zeros((B, Hh, g.NB), dtype=np.float64)
@@ -101,10 +101,10 @@ def aggregation_score(x: np.ndarray, grid: Sequence[int], block: Sequence[int]) 
 
 def scheme_scores(q: np.ndarray, k: np.ndarray, grid: Sequence[int],
                   candidates: Sequence[Sequence[int]]) -> np.ndarray:
-    """R13: score[c, b, h] = AS(Q | c) + AS(K | c), float64."""
+    """R19: score[c, b, h] = AS(Q | c) + AS(K | c), float64."""
     return np.stack([aggregation_score(q, grid, c) + aggregation_score(k, grid, c) for c in candidates])
 
 
 def select_scheme(scores: np.ndarray) -> np.ndarray:
-    """R14: per (batch, head), the first candidate with the highest score."""
+    """R20: per (batch, head), the first candidate with the highest score."""
     return np.argmax(scores, axis=0).astype(np.int32)

@@ -204,3 +204,71 @@ def test_scheme_entry_error_paths(lib):
     assert lib.vsa_sics(None, ctypes.byref(shape), FAKE, None) == _lib.VSA_ERR_INVALID_ARG
     bad = VsaShape(1, 1, 96, 4, 8, 8, 2, 4, 8, 0)
     assert lib.vsa_sics(FAKE, ctypes.byref(bad), FAKE, None) == _lib.VSA_ERR_UNSUPPORTED
+
+
+def _select(mode, vals, window_t=-1, sink=0, scale=0.0):
+    arr = (ctypes.c_float * len(vals))(*vals)
+    sel = _lib.VsaSelect(mode, len(vals), ctypes.cast(arr, ctypes.POINTER(ctypes.c_float)), window_t, sink, scale)
+    return sel, arr
+
+
+def _query_select(lib, shape, sel):
+    rl, cap, pws = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
+    st = lib.vsa_query_select(ctypes.byref(shape), ctypes.byref(sel), ctypes.byref(rl), ctypes.byref(cap),
+                              ctypes.byref(pws))
+    return st, rl.value, cap.value, pws.value
+
+
+@pytest.mark.parametrize("mode,vals,window_t,sink", [
+    (_lib.VSA_TOPK, [0.2], -1, 0), (_lib.VSA_TOPK, [0.2], -1, 3), (_lib.VSA_TOPK, [0.1, 0.5], 1, 2),
+    (_lib.VSA_TOPP, [0.5], -1, 0), (_lib.VSA_TOPP, [0.9, 0.1], 0, 4)])
+def test_query_select_capacity_bounds_oracle(lib, mode, vals, window_t, sink):
+    """The capacity vsa_query_select reports holds the oracle's index (exact
+    for Top-K without window and sinks), and agrees with vsa_query where the
+    two overlap."""
+    from oracle import select_oracle as P
+    w = W.custom("sel", 1, 2, 64, (9, 14, 20), (4, 4, 8), "f32", 0.5, -1, "iid")
+    shape = _shape(w)
+    sel, _keep = _select(mode, vals, window_t, sink)
+    st, rl, cap, pws = _query_select(lib, shape, sel)
+    assert st == 0
+    inp = W.generate(w, seed=2)
+    rp, ci, info = P.plan_select(inp["q"], inp["k"], w.grid, w.block, "topk" if mode == 0 else "topp",
+                                 vals, window_t, sink)
+    assert rl == len(rp)
+    assert cap >= len(ci)
+    if mode == _lib.VSA_TOPK and window_t < 0 and sink == 0:
+        assert cap == len(ci)
+        st2, rl2, cap2, pws2, _ = _query(lib, shape, vals, window_t)
+        assert (st2, rl2, cap2, pws2) == (0, rl, cap, pws)
+    if mode == _lib.VSA_TOPP:
+        assert cap == (len(rp) - 1) * info["geometry"].NB
+
+
+def test_select_entry_error_paths(lib):
+    w = W.WORKLOADS["wan13b"]
+    shape = _shape(w)
+    NB = O.geometry(w.grid, w.block).NB
+    ok, _k1 = _select(_lib.VSA_TOPP, [0.5])
+    st, rl, cap, pws = _query_select(lib, shape, ok)
+    assert st == 0 and cap == 12 * NB * NB
+    for bad in (_select(2, [0.5]), _select(_lib.VSA_TOPP, [0.0]), _select(_lib.VSA_TOPP, [1.5]),
+                _select(_lib.VSA_TOPP, [float("nan")]), _select(_lib.VSA_TOPP, [0.5, 0.5]),
+                _select(_lib.VSA_TOPP, [0.5], sink=-1), _select(_lib.VSA_TOPP, [0.5], sink=NB + 1),
+                _select(_lib.VSA_TOPP, [0.5], scale=-1.0), _select(_lib.VSA_TOPP, [0.5], scale=float("inf")),
+                _select(_lib.VSA_TOPK, [0.5], window_t=-2)):
+        assert _query_select(lib, shape, bad[0])[0] == _lib.VSA_ERR_INVALID_ARG
+    assert lib.vsa_query_select(ctypes.byref(shape), None, None, None, None) == _lib.VSA_ERR_INVALID_ARG
+    assert _query_select(lib, shape, _select(_lib.VSA_TOPP, [0.5], sink=NB)[0])[0] == 0
+
+    def call(q=FAKE, cap_=cap, ws=FAKE, ws_bytes=pws, sel=ok, rp=FAKE):
+        idx = VsaIndex(shape, 0, 0, rp, FAKE, cap_)
+        return lib.vsa_plan_select(q, FAKE, ctypes.byref(shape), ctypes.byref(sel), ctypes.byref(idx), ws,
+                                   ws_bytes, None)
+
+    assert call(q=None) == _lib.VSA_ERR_INVALID_ARG
+    assert call(ws=None) == _lib.VSA_ERR_INVALID_ARG
+    assert call(rp=None) == _lib.VSA_ERR_INVALID_ARG
+    assert call(cap_=cap - 1) == _lib.VSA_ERR_CAPACITY
+    assert call(ws_bytes=pws - 1) == _lib.VSA_ERR_WORKSPACE
+    assert call(sel=_select(_lib.VSA_TOPP, [2.0])[0]) == _lib.VSA_ERR_INVALID_ARG

@@ -5,7 +5,7 @@ oracle (Algorithm 1).
 Bar: SICS and aggregation scores within rtol 1e-4 (atol 1e-3) of the
 oracle -- the kernel accumulates unit vectors in float32, a relative error
 near 1e-6 at these sizes; the chosen scheme must be an argmax of the
-oracle's scores within that bound (a float32 decision, reading R14).
+oracle's scores within that bound (a float32 decision, reading R20).
 """
 import sys
 
@@ -55,7 +55,7 @@ def test_sics_small(vsa, w):
     _say(f"[gpu] sics {w.name} grid={w.grid} block={w.block} D={w.D} {w.dtype}")
     inp = W.generate(w, seed=4)
     q = inp["q"].copy()
-    q[0, 0, 5] = 0.0   # a zero token: adds nothing (reading R12)
+    q[0, 0, 5] = 0.0   # a zero token: adds nothing (reading R18)
     got = vsa.sics(_dev(q, w), w.grid, w.block).cpu().numpy()
     ref = S.block_sics(q, O.geometry(w.grid, w.block))
     np.testing.assert_allclose(got, ref, rtol=RTOL, atol=ATOL)

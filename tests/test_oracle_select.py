@@ -1,6 +1,6 @@
 """Pins for the selection-variant oracle (SPADE 3.1 Top-K/Top-P mode and
 attention-sink length, 3.3 Top-P filtering and union with the sink mask;
-readings R15-R18).  Each checks the oracle against something other than its
+readings R21-R24).  Each checks the oracle against something other than its
 own formula: a hand-worked example, brute force over all subsets of tiny
 rows, closed forms of uniform and two-level rows, limits that reduce to
 argmax or to the whole row, nesting in p, shift invariance of the softmax,
@@ -61,7 +61,7 @@ def _subset_mass(prob, ids):
 
 @pytest.mark.parametrize("seed", range(12))
 def test_brute_force_smallest_covering_set(seed):
-    """R15 as a set statement: the kept blocks form a smallest set whose
+    """R21 as a set statement: the kept blocks form a smallest set whose
     probability reaches p, of the largest mass among sets of that size, and
     among those the one with the lowest ids."""
     rng = np.random.default_rng(seed)

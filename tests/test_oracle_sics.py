@@ -59,7 +59,7 @@ def test_special_cases():
 
 
 def test_zero_token_reading():
-    """R12: a zero token contributes nothing, not even its diagonal term."""
+    """R18: a zero token contributes nothing, not even its diagonal term."""
     rng = np.random.default_rng(6)
     x = rng.standard_normal((9, 5))
     with_zero = np.concatenate([x[:4], np.zeros((1, 5)), x[4:]])
@@ -76,7 +76,7 @@ def test_hand_example():
 def test_block_sics_uses_block_tokens_and_ragged_edges():
     """Eq. 3 per block: each block's SICS is over exactly its own tokens
     (checked against the closed form on the raster tokens of its box);
-    cut-short edge blocks use their valid tokens (R11)."""
+    cut-short edge blocks use their valid tokens (R17)."""
     grid, block = (3, 5, 6), (2, 4, 4)
     g = O.geometry(grid, block)
     x = np.random.default_rng(7).standard_normal((1, 2, int(np.prod(grid)), 8))
