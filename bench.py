@@ -119,20 +119,20 @@ def cpu_baseline(inp, w, row_ptr, col_idx, sizes, step_flops, budget_s=20.0):
             "seconds_per_step": t_step}
 
 
-def time_select(vsa, lib, _lib, q, k, v, o, w, mode, val, sink, stream, sizes, reps=20):
+def time_select(vsa, lib, _lib, q, k, v, o, w, mode, val, sink, stream, sizes, estimator="mean", reps=20):
     """Mean plan time of vsa_plan_select for one selection, and attention
     over the index it produces (both timed with events on the stream)."""
     import ctypes
 
     import torch
     shape = vsa._shape_of(q, w.grid, w.block)
-    rl, cap, pws = vsa.query_select(shape, mode, [val], w.window_t, sink)
+    rl, cap, pws = vsa.query_select(shape, mode, [val], w.window_t, sink, None, estimator)
     dev = q.device
     row_ptr = torch.empty(rl, dtype=torch.int32, device=dev)
     col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
     ws = torch.empty(max(pws, 1), dtype=torch.uint8, device=dev)
     cidx = _lib.VsaIndex(shape, 0, 0, ctypes.c_void_p(row_ptr.data_ptr()), ctypes.c_void_p(col_idx.data_ptr()), cap)
-    sel, _vals = vsa._select(shape, mode, [val], w.window_t, sink, None)
+    sel, _vals = vsa._select(shape, mode, [val], w.window_t, sink, None, estimator)
     sp = ctypes.c_void_p(stream.cuda_stream)
     qp, kp, vp, op = (ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, o))
 
@@ -161,7 +161,7 @@ def time_select(vsa, lib, _lib, q, k, v, o, w, mode, val, sink, stream, sizes, r
     ci = col_idx.cpu().numpy().astype(np.int64)[: int(rp[-1])]
     flops = executed_flops(rp, ci, sizes, w.D)
     lens = np.diff(rp)
-    return {"mode": mode, "value": val, "sink": sink, "window_t": w.window_t,
+    return {"estimator": estimator, "mode": mode, "value": val, "sink": sink, "window_t": w.window_t,
             "plan_ms": round(plan_ms, 4), "attn_ms": round(attn_ms, 4),
             "attn_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 2),
             "nnz_blocks": int(rp[-1]), "density": round(float(rp[-1]) / (len(lens) * len(sizes)), 4),
@@ -329,8 +329,9 @@ def main():
     # and followed by attention over the index it produced.
     if w.dtype == "bf16" and w.name == "wan13b":
         result["select_variants"] = [
-            time_select(vsa, lib, _lib, q, k, v, o, w, mode, val, sink, stream, sizes)
-            for mode, val, sink in (("topp", 0.25, 2), ("topk", 0.2, 2))]
+            time_select(vsa, lib, _lib, q, k, v, o, w, mode, val, sink, stream, sizes, est)
+            for est, mode, val, sink in (("mean", "topp", 0.25, 2), ("mean", "topk", 0.2, 2),
+                                         ("dsa", "topk", 0.2, 0), ("dsa2", "topk", 0.2, 0))]
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inp, w, rp, ci, sizes, flops, a.cpu_budget)

@@ -24,7 +24,7 @@ from . import _lib
 from ._lib import VsaError, VsaIndex, VsaSelect, VsaShape, check, load
 
 __all__ = ["plan", "plan_select", "attn", "query", "query_select", "permute", "unpermute",
-           "centroids", "centroid_scores", "sics", "select_scheme", "Index", "VsaError", "load"]
+           "centroids", "centroid_scores", "estimate", "sics", "select_scheme", "Index", "VsaError", "load"]
 
 _DTYPES = {torch.bfloat16: _lib.VSA_BF16, torch.float32: _lib.VSA_F32}
 
@@ -117,22 +117,30 @@ def plan(q: torch.Tensor, k: torch.Tensor, grid, block, density: Union[float, Se
 
 
 _MODES = {"topk": _lib.VSA_TOPK, "topp": _lib.VSA_TOPP}
+_ESTIMATORS = {"mean": _lib.VSA_EST_MEAN, "dsa": _lib.VSA_EST_DSA, "dsa2": _lib.VSA_EST_DSA2}
 
 
-def _select(shape: VsaShape, mode: str, value, window_t: int, sink: int, scale: Optional[float]):
+def _estimator(name: str) -> int:
+    if name not in _ESTIMATORS:
+        raise ValueError(f"estimator must be one of {sorted(_ESTIMATORS)}")
+    return _ESTIMATORS[name]
+
+
+def _select(shape: VsaShape, mode: str, value, window_t: int, sink: int, scale: Optional[float],
+            estimator: str = "mean"):
     if mode not in _MODES:
         raise ValueError(f"mode must be one of {sorted(_MODES)}")
     vals, n = _densities(value, shape.heads)
     sel = VsaSelect(_MODES[mode], n, ctypes.cast(vals, ctypes.POINTER(ctypes.c_float)), int(window_t),
-                    int(sink), 0.0 if scale is None else float(scale))
+                    int(sink), 0.0 if scale is None else float(scale), _estimator(estimator))
     return sel, vals   # keep vals alive with sel
 
 
 def query_select(shape: VsaShape, mode: str, value, window_t: int = -1, sink: int = 0,
-                 scale: Optional[float] = None):
+                 scale: Optional[float] = None, estimator: str = "mean"):
     """(row_ptr_len, col_capacity, plan_ws_bytes) for plan_select."""
     lib = load()
-    sel, _vals = _select(shape, mode, value, window_t, sink, scale)
+    sel, _vals = _select(shape, mode, value, window_t, sink, scale, estimator)
     rl, cap, pws = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
     check(lib.vsa_query_select(ctypes.byref(shape), ctypes.byref(sel), ctypes.byref(rl),
                                ctypes.byref(cap), ctypes.byref(pws)), "vsa_query_select")
@@ -141,22 +149,23 @@ def query_select(shape: VsaShape, mode: str, value, window_t: int = -1, sink: in
 
 def plan_select(q: torch.Tensor, k: torch.Tensor, grid, block, mode: str,
                 value: Union[float, Sequence[float]], window_t: int = -1, sink: int = 0,
-                scale: Optional[float] = None) -> Index:
-    """Block means -> centroid scores -> per-row Top-K (value = keep rate)
-    or Top-P (value = cumulative threshold p of softmax(scale * scores)),
-    united with the temporal window and the first `sink` key blocks -> CSR."""
+                scale: Optional[float] = None, estimator: str = "mean") -> Index:
+    """Block summaries -> estimator scores ("mean", "dsa" or "dsa2") ->
+    per-row Top-K (value = keep rate) or Top-P (value = cumulative
+    threshold p of softmax(scale * scores)), united with the temporal window
+    and the first `sink` key blocks -> CSR."""
     lib = load()
     shape = _shape_of(q, grid, block)
     if k.shape != q.shape or k.dtype != q.dtype or not k.is_contiguous():
         raise ValueError("k must match q")
-    rl, cap, pws = query_select(shape, mode, value, window_t, sink, scale)
+    rl, cap, pws = query_select(shape, mode, value, window_t, sink, scale, estimator)
     dev = q.device
     row_ptr = torch.empty(rl, dtype=torch.int32, device=dev)
     col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
     ws = torch.empty(max(pws, 1), dtype=torch.uint8, device=dev)
     cidx = VsaIndex(shape, 0, 0, ctypes.c_void_p(row_ptr.data_ptr()),
                     ctypes.c_void_p(col_idx.data_ptr()), cap)
-    sel, _vals = _select(shape, mode, value, window_t, sink, scale)
+    sel, _vals = _select(shape, mode, value, window_t, sink, scale, estimator)
     check(lib.vsa_plan_select(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
                               ctypes.byref(shape), ctypes.byref(sel), ctypes.byref(cidx),
                               ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(q)), "vsa_plan_select")
@@ -233,6 +242,23 @@ def centroid_scores(qc: torch.Tensor, kc: torch.Tensor, grid, block, dtype=torch
     check(lib.vsa_centroid_scores(ctypes.c_void_p(qc.data_ptr()), ctypes.c_void_p(kc.data_ptr()),
                                   ctypes.byref(s), ctypes.c_void_p(out.data_ptr()), _stream(qc)),
           "vsa_centroid_scores")
+    return out
+
+
+def estimate(q: torch.Tensor, k: torch.Tensor, grid, block, estimator: str = "mean") -> torch.Tensor:
+    """Inter-block importance matrix float32 [B, heads, NB, NB] of an
+    estimator, as vsa_plan_select ranks it."""
+    lib = load()
+    s = _shape_of(q, grid, block)
+    if k.shape != q.shape or k.dtype != q.dtype or not k.is_contiguous():
+        raise ValueError("k must match q")
+    _, _, pws = query_select(s, "topk", 1.0, estimator=estimator)
+    ws = torch.empty(max(pws, 1), dtype=torch.uint8, device=q.device)
+    nb = math.prod(-(-int(n) // int(b)) for n, b in zip(grid, block))
+    out = torch.empty((s.B, s.heads, nb, nb), dtype=torch.float32, device=q.device)
+    check(lib.vsa_estimate(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.byref(s),
+                           _estimator(estimator), ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                           ws.numel(), _stream(q)), "vsa_estimate")
     return out
 
 

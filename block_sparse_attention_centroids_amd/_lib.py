@@ -21,6 +21,10 @@ VSA_F32 = 1
 VSA_TOPK = 0
 VSA_TOPP = 1
 
+VSA_EST_MEAN = 0
+VSA_EST_DSA = 1
+VSA_EST_DSA2 = 2
+
 
 class VsaShape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("heads", ctypes.c_int32), ("D", ctypes.c_int32),
@@ -38,7 +42,7 @@ class VsaIndex(ctypes.Structure):
 class VsaSelect(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("n_value", ctypes.c_int32),
                 ("value", ctypes.POINTER(ctypes.c_float)), ("window_t", ctypes.c_int32),
-                ("sink", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("sink", ctypes.c_int32), ("scale", ctypes.c_float), ("estimator", ctypes.c_int32)]
 
 
 class VsaError(RuntimeError):
@@ -51,7 +55,7 @@ _lib = None
 
 EXPORTS = ("vsa_query", "vsa_plan", "vsa_attn", "vsa_permute", "vsa_unpermute",
            "vsa_centroids", "vsa_centroid_scores", "vsa_sics", "vsa_scheme_workspace",
-           "vsa_select_scheme", "vsa_query_select", "vsa_plan_select", "vsa_status_str")
+           "vsa_select_scheme", "vsa_query_select", "vsa_plan_select", "vsa_estimate", "vsa_status_str")
 
 
 def load() -> ctypes.CDLL:
@@ -87,6 +91,7 @@ def load() -> ctypes.CDLL:
                                      ctypes.POINTER(ctypes.c_size_t)]
     lib.vsa_plan_select.argtypes = [P, P, ctypes.POINTER(VsaShape), ctypes.POINTER(VsaSelect),
                                     ctypes.POINTER(VsaIndex), P, ctypes.c_size_t, P]
+    lib.vsa_estimate.argtypes = [P, P, ctypes.POINTER(VsaShape), I, P, P, ctypes.c_size_t, P]
     for name in EXPORTS[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     lib.vsa_status_str.argtypes = [ctypes.c_int]

@@ -41,6 +41,26 @@ bool same_shape(const vsa_shape& a, const vsa_shape& b) {
 
 vsa_status hip_status(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_HIP; }
 
+// Enqueue the block summaries of the estimator into the workspace regions
+// ps.off_sum and describe them for the scoring kernels.
+hipError_t summarize(const void* q, const void* k, const vsa_shape* shape, const PlanSizes& ps, char* w,
+                     const DGeo& dg, int BH, hipStream_t st, Summaries* sm) {
+  float* s0 = reinterpret_cast<float*>(w + ps.off_sum[0]);
+  float* s1 = reinterpret_cast<float*>(w + ps.off_sum[1]);
+  float* s2 = ps.n_sum > 2 ? reinterpret_cast<float*>(w + ps.off_sum[2]) : nullptr;
+  float* s3 = ps.n_sum > 3 ? reinterpret_cast<float*>(w + ps.off_sum[3]) : nullptr;
+  if (ps.estimator == VSA_EST_MEAN) {
+    *sm = Summaries{s0, nullptr, s1, nullptr};
+    return launch_pool(q, s0, k, s1, shape->dtype, shape->D, dg, BH, st);
+  }
+  if (ps.estimator == VSA_EST_DSA) {
+    *sm = Summaries{s0, nullptr, s1, s2};
+    return launch_extremes(q, s0, nullptr, 1, k, s1, s2, 0, shape->dtype, shape->D, dg, BH, st);
+  }
+  *sm = Summaries{s0, s1, s2, s3};
+  return launch_extremes(q, s0, s1, 0, k, s2, s3, 0, shape->dtype, shape->D, dg, BH, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -105,8 +125,6 @@ vsa_status vsa_plan_select(const void* q, const void* k, const vsa_shape* shape,
     const int BH = shape->B * shape->heads;
     hipStream_t st_ = reinterpret_cast<hipStream_t>(stream);
     char* w = static_cast<char*>(ws);
-    float* qc = reinterpret_cast<float*>(w + ps.off_qc);
-    float* kc = reinterpret_cast<float*>(w + ps.off_kc);
 
     SelectArgs sa;
     std::memset(&sa, 0, sizeof(sa));
@@ -136,9 +154,10 @@ vsa_status vsa_plan_select(const void* q, const void* k, const vsa_shape* shape,
     index->nb = g.NB;
     index->window_t = sel->window_t;
 
-    hipError_t e = launch_pool(q, qc, k, kc, shape->dtype, shape->D, dg, BH, st_);
+    Summaries sm;
+    hipError_t e = summarize(q, k, shape, ps, w, dg, BH, st_, &sm);
     if (e == hipSuccess)
-      e = launch_score_select(qc, kc, dg, shape->D, shape->heads, BH, sa, index->row_ptr,
+      e = launch_score_select(sm, ps.estimator, dg, shape->D, shape->heads, BH, sa, index->row_ptr,
                               index->col_idx, counts, bits, st_);
     if (e == hipSuccess && ps.bitmap)
       e = launch_scan_fill(counts, bits, index->row_ptr, index->col_idx, ps.rows, ps.words, g.NB,
@@ -159,7 +178,40 @@ vsa_status vsa_plan(const void* q, const void* k, const vsa_shape* shape, const 
   sel.window_t = window_t;
   sel.sink = 0;
   sel.scale = 0.0f;
+  sel.estimator = VSA_EST_MEAN;
   return vsa_plan_select(q, k, shape, &sel, index, ws, ws_bytes, stream);
+}
+
+vsa_status vsa_estimate(const void* q, const void* k, const vsa_shape* shape, int estimator, float* out,
+                        void* ws, size_t ws_bytes, void* stream) {
+  try {
+    if (!q || !k || !out || !ws) return VSA_ERR_INVALID_ARG;
+    const float one = 1.0f;
+    vsa_select sel;
+    sel.mode = VSA_TOPK;
+    sel.n_value = 1;
+    sel.value = &one;
+    sel.window_t = -1;
+    sel.sink = 0;
+    sel.scale = 0.0f;
+    sel.estimator = estimator;
+    PlanSizes ps;
+    vsa_status st = select_sizes(shape, &sel, &ps);
+    if (st != VSA_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(ws)) return VSA_ERR_INVALID_ARG;
+    size_t need = ps.off_sum[ps.n_sum - 1] + align256(size_t(ps.rows) * shape->D * sizeof(float));
+    if (ws_bytes < need) return VSA_ERR_WORKSPACE;
+    const Geo g = make_geo(*shape);
+    const DGeo dg = to_dgeo(g);
+    const int BH = shape->B * shape->heads;
+    hipStream_t st_ = reinterpret_cast<hipStream_t>(stream);
+    Summaries sm;
+    hipError_t e = summarize(q, k, shape, ps, static_cast<char*>(ws), dg, BH, st_, &sm);
+    if (e == hipSuccess) e = launch_scores(sm, ps.estimator, out, g.NB, shape->D, BH, st_);
+    return hip_status(e);
+  } catch (...) {
+    return VSA_ERR_INVALID_ARG;
+  }
 }
 
 vsa_status vsa_attn(const void* q, const void* k, const void* v, const vsa_index* index,
@@ -219,7 +271,8 @@ vsa_status vsa_centroid_scores(const float* qc, const float* kc, const vsa_shape
   if (st != VSA_OK) return st;
   if (!qc || !kc || !out || !aligned16(qc) || !aligned16(kc)) return VSA_ERR_INVALID_ARG;
   const Geo g = make_geo(*shape);
-  return hip_status(launch_scores(qc, kc, out, g.NB, shape->D, shape->B * shape->heads,
+  return hip_status(launch_scores(Summaries{qc, nullptr, kc, nullptr}, VSA_EST_MEAN, out, g.NB, shape->D,
+                                  shape->B * shape->heads,
                                   reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -1,8 +1,9 @@
-// Planning kernels for gfx950: block means (the summarizer), centroid dot
-// products (the inter-estimator) with per-row Top-K or Top-P selection
+// Planning kernels for gfx950: block means or extremes (the summarizers),
+// their inter-estimators (mean dot product, DSA, DSA2) with per-row Top-K or
+// Top-P selection
 // united with the local temporal window and the attention-sink blocks, and
 // the CSR scan/fill used when rows vary in length.  SPADE (arXiv
-// 2608.03335) 3.1 Fig. 4(c) and the vDiT-SSR utility parameters, and 3.3.
+// 2608.03335) 3.1 Fig. 4 and the vDiT-SSR utility parameters, and 3.3.
 //
 // This file is built with -ffp-contract=off and every product/sum uses the
 // explicitly rounded intrinsics, so the arithmetic is the fixed float32
@@ -108,6 +109,81 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ x0, flo
   for (int c = 0; c < C; ++c) o[c] = __fdiv_rn(acc[c], (float)n);
 }
 
+// ---------------------------------------------------------------------------
+// Block extremes (the max/min summarizer).  Same walk as pool_kernel; a
+// load past the block's last token is skipped rather than added.  For a
+// tensor with `mid` set the query midpoint fl(fl(max + min) * 0.5) goes to
+// omax and omin is not written.  max and min are exact.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void extremes_kernel(const T* __restrict__ x0, float* __restrict__ omax0,
+                                                       float* __restrict__ omin0, int mid0,
+                                                       const T* __restrict__ x1, float* __restrict__ omax1,
+                                                       float* __restrict__ omin1, int mid1, DGeo g, int nitems) {
+  constexpr int C = D / 64;
+  constexpr int PF = 32;
+  constexpr int ROWB = D * (int)sizeof(T);
+  const int wave = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + wave;
+  if (item >= nitems) return;
+  const T* x = blockIdx.y ? x1 : x0;
+  float* omax = blockIdx.y ? omax1 : omax0;
+  float* omin = blockIdx.y ? omin1 : omin0;
+  const int mid = blockIdx.y ? mid1 : mid0;
+  const int bh = item / g.NB, j = item - bh * g.NB;
+  const Box b = block_box(g, j);
+  const int n = uniform_i(b.n());
+  const __amdgpu_buffer_rsrc_t rs = plan_rsrc(x + (size_t)bh * g.N * D, (uint32_t)g.N * ROWB);
+  const int voff = lane * C * (int)sizeof(T);
+  int soff = uniform_i(((b.t0 * g.H + b.h0) * g.W + b.w0) * ROWB);
+  int uh = 0, uw = 0;
+  const int ew = uniform_i(b.ew), eh = uniform_i(b.eh);
+  const int wrap_w = uniform_i((g.W - b.ew) * ROWB), wrap_h = uniform_i((g.H - b.eh) * g.W * ROWB);
+  float mx[C], mn[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    mx[c] = -INFINITY;
+    mn[c] = INFINITY;
+  }
+  for (int u0 = 0; u0 < n; u0 += PF) {
+    float v[PF][C];
+#pragma unroll
+    for (int e = 0; e < PF; ++e) {
+      load_token<T, C>(rs, voff, u0 + e < n ? soff : (int)0x80000000, v[e]);
+      soff += ROWB;
+      if (++uw == ew) {
+        uw = 0;
+        soff += wrap_w;
+        if (++uh == eh) {
+          uh = 0;
+          soff += wrap_h;
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < PF; ++e) {
+      const bool ok = u0 + e < n;
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        mx[c] = ok ? fmaxf(mx[c], v[e][c]) : mx[c];
+        mn[c] = ok ? fminf(mn[c], v[e][c]) : mn[c];
+      }
+    }
+  }
+  float* oa = omax + (size_t)item * D + lane * C;
+  if (mid) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) oa[c] = __fmul_rn(__fadd_rn(mx[c], mn[c]), 0.5f);
+  } else {
+    float* ob = omin + (size_t)item * D + lane * C;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      oa[c] = mx[c];
+      ob[c] = mn[c];
+    }
+  }
+}
+
 // Scores of RT query blocks (rows i0..i0+RT-1, clamped) against key block j.
 // The query means are wave-uniform, so they come through scalar loads.
 template <int RT>
@@ -124,6 +200,48 @@ __device__ inline void score_column(const float* __restrict__ qrows, const float
       acc[r] = __fadd_rn(acc[r], __fmul_rn(qv.y, kv.y));
       acc[r] = __fadd_rn(acc[r], __fmul_rn(qv.z, kv.z));
       acc[r] = __fadd_rn(acc[r], __fmul_rn(qv.w, kv.w));
+    }
+  }
+}
+
+// Scores of RT query-block summaries against key block j for an estimator
+// (EST 0: mean, 1: DSA, 2: DSA2).  qa/qb are the query summaries (mean, or
+// midpoint, or max/min), ka/kb the key summaries (mean, or max/min).  DSA
+// adds, channel by channel, the larger of the two rounded products of the
+// midpoint with the key box corners; DSA2 the largest of the four corner
+// products; the sums run over channels in order from +0.
+template <int EST, int RT>
+__device__ inline void est_column(const float* __restrict__ qa, const float* __restrict__ qb,
+                                  const float* __restrict__ ka, const float* __restrict__ kb, int D,
+                                  float (&acc)[RT]) {
+  if constexpr (EST == 0) {
+    score_column<RT>(qa, ka, D, acc);
+  } else {
+#pragma unroll
+    for (int r = 0; r < RT; ++r) acc[r] = 0.0f;
+    for (int d = 0; d < D; d += 4) {
+      const float4 kA = *reinterpret_cast<const float4*>(ka + d);
+      const float4 kB = *reinterpret_cast<const float4*>(kb + d);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const float4 qA = *reinterpret_cast<const float4*>(qa + (size_t)r * D + d);
+        if constexpr (EST == 1) {
+          acc[r] = __fadd_rn(acc[r], fmaxf(__fmul_rn(qA.x, kA.x), __fmul_rn(qA.x, kB.x)));
+          acc[r] = __fadd_rn(acc[r], fmaxf(__fmul_rn(qA.y, kA.y), __fmul_rn(qA.y, kB.y)));
+          acc[r] = __fadd_rn(acc[r], fmaxf(__fmul_rn(qA.z, kA.z), __fmul_rn(qA.z, kB.z)));
+          acc[r] = __fadd_rn(acc[r], fmaxf(__fmul_rn(qA.w, kA.w), __fmul_rn(qA.w, kB.w)));
+        } else {
+          const float4 qB = *reinterpret_cast<const float4*>(qb + (size_t)r * D + d);
+          acc[r] = __fadd_rn(acc[r], fmaxf(fmaxf(__fmul_rn(qA.x, kA.x), __fmul_rn(qA.x, kB.x)),
+                                           fmaxf(__fmul_rn(qB.x, kA.x), __fmul_rn(qB.x, kB.x))));
+          acc[r] = __fadd_rn(acc[r], fmaxf(fmaxf(__fmul_rn(qA.y, kA.y), __fmul_rn(qA.y, kB.y)),
+                                           fmaxf(__fmul_rn(qB.y, kA.y), __fmul_rn(qB.y, kB.y))));
+          acc[r] = __fadd_rn(acc[r], fmaxf(fmaxf(__fmul_rn(qA.z, kA.z), __fmul_rn(qA.z, kB.z)),
+                                           fmaxf(__fmul_rn(qB.z, kA.z), __fmul_rn(qB.z, kB.z))));
+          acc[r] = __fadd_rn(acc[r], fmaxf(fmaxf(__fmul_rn(qA.w, kA.w), __fmul_rn(qA.w, kB.w)),
+                                           fmaxf(__fmul_rn(qB.w, kA.w), __fmul_rn(qB.w, kB.w))));
+        }
+      }
     }
   }
 }
@@ -326,9 +444,9 @@ __device__ inline void topp_cut_lds(const uint32_t* keys, int NB, int lane, floa
 // ties at the threshold going to the lowest ids, united with the window and
 // the sink blocks.
 // ---------------------------------------------------------------------------
-template <int RT, bool TOPP>
+template <int RT, bool TOPP, int EST>
 __global__ __launch_bounds__(256) void score_select_kernel(
-    const float* __restrict__ qc, const float* __restrict__ kc, DGeo g, int D, int heads,
+    Summaries sm, DGeo g, int D, int heads,
     SelectArgs sa, int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
     int32_t* __restrict__ counts, uint64_t* __restrict__ bits) {
   extern __shared__ uint32_t smem[];   // [RT][NB] keys
@@ -338,11 +456,16 @@ __global__ __launch_bounds__(256) void score_select_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int rows_here = min(RT, NB - i0);
   // Phase 1: scores.  Rows past NB reuse the last valid row (never emitted).
-  const float* kbase = kc + (size_t)bh * NB * D;
+  const size_t head = (size_t)bh * NB * D;
+  const float* qa = sm.qa + head;
+  const float* qb = EST == 2 ? sm.qb + head : nullptr;
+  const float* ka = sm.ka + head;
+  const float* kb = EST != 0 ? sm.kb + head : nullptr;
   if (rows_here == RT) {
     for (int j = tid; j < NB; j += 256) {
       float acc[RT];
-      score_column<RT>(qc + ((size_t)bh * NB + i0) * D, kbase + (size_t)j * D, D, acc);
+      est_column<EST, RT>(qa + (size_t)i0 * D, qb + (EST == 2 ? (size_t)i0 * D : 0), ka + (size_t)j * D,
+                          kb + (EST != 0 ? (size_t)j * D : 0), D, acc);
 #pragma unroll
       for (int r = 0; r < RT; ++r) smem[r * NB + j] = order_key(acc[r]);
     }
@@ -350,7 +473,9 @@ __global__ __launch_bounds__(256) void score_select_kernel(
     for (int j = tid; j < NB; j += 256) {
       for (int r = 0; r < rows_here; ++r) {
         float acc[1];
-        score_column<1>(qc + ((size_t)bh * NB + i0 + r) * D, kbase + (size_t)j * D, D, acc);
+        const size_t qi = (size_t)(i0 + r) * D;
+        est_column<EST, 1>(qa + qi, qb + (EST == 2 ? qi : 0), ka + (size_t)j * D,
+                           kb + (EST != 0 ? (size_t)j * D : 0), D, acc);
         smem[r * NB + j] = order_key(acc[0]);
       }
     }
@@ -458,14 +583,17 @@ __global__ __launch_bounds__(256) void fill_kernel(const uint64_t* __restrict__ 
 }
 
 // Full score matrix (the inter-estimator alone), same order as above.
-__global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ qc,
-                                                     const float* __restrict__ kc,
-                                                     float* __restrict__ out, int NB, int D) {
+template <int EST>
+__global__ __launch_bounds__(256) void scores_kernel(Summaries sm, float* __restrict__ out, int NB, int D) {
   const int bh = blockIdx.y;
   const int i = blockIdx.x;
+  const size_t head = (size_t)bh * NB * D;
+  const size_t qi = head + (size_t)i * D;
   for (int j = threadIdx.x; j < NB; j += 256) {
     float acc[1];
-    score_column<1>(qc + ((size_t)bh * NB + i) * D, kc + ((size_t)bh * NB + j) * D, D, acc);
+    const size_t kj = head + (size_t)j * D;
+    est_column<EST, 1>(sm.qa + qi, EST == 2 ? sm.qb + qi : nullptr, sm.ka + kj, EST != 0 ? sm.kb + kj : nullptr,
+                       D, acc);
     out[((size_t)bh * NB + i) * NB + j] = acc[0];
   }
 }
@@ -503,28 +631,40 @@ int select_rows_per_block(int NB) {
   return 1;
 }
 
-template <bool TOPP>
-void launch_score_select_t(int RT, dim3 grid, dim3 block, size_t lds, hipStream_t st, const float* qc,
-                           const float* kc, const DGeo& g, int D, int heads, const SelectArgs& sa,
-                           int32_t* row_ptr, int32_t* col_idx, int32_t* counts, uint64_t* bits) {
+template <bool TOPP, int EST>
+void launch_score_select_t(int RT, dim3 grid, dim3 block, size_t lds, hipStream_t st, const Summaries& sm,
+                           const DGeo& g, int D, int heads, const SelectArgs& sa, int32_t* row_ptr,
+                           int32_t* col_idx, int32_t* counts, uint64_t* bits) {
   switch (RT) {
-    case 8: hipLaunchKernelGGL((score_select_kernel<8, TOPP>), grid, block, lds, st, qc, kc, g, D, heads, sa, row_ptr, col_idx, counts, bits); break;
-    case 4: hipLaunchKernelGGL((score_select_kernel<4, TOPP>), grid, block, lds, st, qc, kc, g, D, heads, sa, row_ptr, col_idx, counts, bits); break;
-    case 2: hipLaunchKernelGGL((score_select_kernel<2, TOPP>), grid, block, lds, st, qc, kc, g, D, heads, sa, row_ptr, col_idx, counts, bits); break;
-    default: hipLaunchKernelGGL((score_select_kernel<1, TOPP>), grid, block, lds, st, qc, kc, g, D, heads, sa, row_ptr, col_idx, counts, bits); break;
+    case 8: hipLaunchKernelGGL((score_select_kernel<8, TOPP, EST>), grid, block, lds, st, sm, g, D, heads, sa, row_ptr, col_idx, counts, bits); break;
+    case 4: hipLaunchKernelGGL((score_select_kernel<4, TOPP, EST>), grid, block, lds, st, sm, g, D, heads, sa, row_ptr, col_idx, counts, bits); break;
+    case 2: hipLaunchKernelGGL((score_select_kernel<2, TOPP, EST>), grid, block, lds, st, sm, g, D, heads, sa, row_ptr, col_idx, counts, bits); break;
+    default: hipLaunchKernelGGL((score_select_kernel<1, TOPP, EST>), grid, block, lds, st, sm, g, D, heads, sa, row_ptr, col_idx, counts, bits); break;
   }
 }
 
-hipError_t launch_score_select(const float* qc, const float* kc, const DGeo& g, int D, int heads,
-                               int BH, const SelectArgs& sa, int32_t* row_ptr, int32_t* col_idx,
-                               int32_t* counts, uint64_t* bits, hipStream_t st) {
+template <int EST>
+void launch_score_select_e(int RT, dim3 grid, dim3 block, size_t lds, hipStream_t st, const Summaries& sm,
+                           const DGeo& g, int D, int heads, const SelectArgs& sa, int32_t* row_ptr,
+                           int32_t* col_idx, int32_t* counts, uint64_t* bits) {
+  if (sa.topp)
+    launch_score_select_t<true, EST>(RT, grid, block, lds, st, sm, g, D, heads, sa, row_ptr, col_idx, counts, bits);
+  else
+    launch_score_select_t<false, EST>(RT, grid, block, lds, st, sm, g, D, heads, sa, row_ptr, col_idx, counts, bits);
+}
+
+hipError_t launch_score_select(const Summaries& sm, int est, const DGeo& g, int D, int heads, int BH,
+                               const SelectArgs& sa, int32_t* row_ptr, int32_t* col_idx, int32_t* counts,
+                               uint64_t* bits, hipStream_t st) {
   const int RT = select_rows_per_block(g.NB);
   dim3 grid((g.NB + RT - 1) / RT, BH), block(256);
   size_t lds = (size_t)RT * g.NB * sizeof(uint32_t);
-  if (sa.topp)
-    launch_score_select_t<true>(RT, grid, block, lds, st, qc, kc, g, D, heads, sa, row_ptr, col_idx, counts, bits);
+  if (est == 1)
+    launch_score_select_e<1>(RT, grid, block, lds, st, sm, g, D, heads, sa, row_ptr, col_idx, counts, bits);
+  else if (est == 2)
+    launch_score_select_e<2>(RT, grid, block, lds, st, sm, g, D, heads, sa, row_ptr, col_idx, counts, bits);
   else
-    launch_score_select_t<false>(RT, grid, block, lds, st, qc, kc, g, D, heads, sa, row_ptr, col_idx, counts, bits);
+    launch_score_select_e<0>(RT, grid, block, lds, st, sm, g, D, heads, sa, row_ptr, col_idx, counts, bits);
   return hipGetLastError();
 }
 
@@ -538,9 +678,35 @@ hipError_t launch_scan_fill(const int32_t* counts, const uint64_t* bits, int32_t
   return hipGetLastError();
 }
 
-hipError_t launch_scores(const float* qc, const float* kc, float* out, int NB, int D, int BH,
-                         hipStream_t st) {
-  hipLaunchKernelGGL(scores_kernel, dim3(NB, BH), dim3(256), 0, st, qc, kc, out, NB, D);
+hipError_t launch_scores(const Summaries& sm, int est, float* out, int NB, int D, int BH, hipStream_t st) {
+  if (est == 1)
+    hipLaunchKernelGGL(scores_kernel<1>, dim3(NB, BH), dim3(256), 0, st, sm, out, NB, D);
+  else if (est == 2)
+    hipLaunchKernelGGL(scores_kernel<2>, dim3(NB, BH), dim3(256), 0, st, sm, out, NB, D);
+  else
+    hipLaunchKernelGGL(scores_kernel<0>, dim3(NB, BH), dim3(256), 0, st, sm, out, NB, D);
+  return hipGetLastError();
+}
+
+hipError_t launch_extremes(const void* x0, float* max0, float* min0, int mid0, const void* x1, float* max1,
+                           float* min1, int mid1, int dtype, int D, const DGeo& g, int BH, hipStream_t st) {
+  const int nitems = BH * g.NB;
+  dim3 grid((nitems + 3) / 4, x1 ? 2 : 1), block(256);
+  if (dtype == 0) {
+    if (D == 128)
+      hipLaunchKernelGGL((extremes_kernel<uint16_t, 128>), grid, block, 0, st, (const uint16_t*)x0, max0, min0, mid0,
+                         (const uint16_t*)x1, max1, min1, mid1, g, nitems);
+    else
+      hipLaunchKernelGGL((extremes_kernel<uint16_t, 64>), grid, block, 0, st, (const uint16_t*)x0, max0, min0, mid0,
+                         (const uint16_t*)x1, max1, min1, mid1, g, nitems);
+  } else {
+    if (D == 128)
+      hipLaunchKernelGGL((extremes_kernel<float, 128>), grid, block, 0, st, (const float*)x0, max0, min0, mid0,
+                         (const float*)x1, max1, min1, mid1, g, nitems);
+    else
+      hipLaunchKernelGGL((extremes_kernel<float, 64>), grid, block, 0, st, (const float*)x0, max0, min0, mid0,
+                         (const float*)x1, max1, min1, mid1, g, nitems);
+  }
   return hipGetLastError();
 }
 

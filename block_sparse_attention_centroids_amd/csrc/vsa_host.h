@@ -93,7 +93,10 @@ struct PlanSizes {
   int64_t rows = 0;          // B*heads*NB
   int64_t capacity = 0;      // col_idx entries needed (an upper bound in bitmap mode)
   size_t ws = 0;             // plan workspace bytes
-  size_t off_qc = 0, off_kc = 0, off_cnt = 0, off_bits = 0;
+  size_t off_sum[4] = {0, 0, 0, 0};   // block summaries (2, 3 or 4 arrays)
+  int n_sum = 2;
+  int estimator = VSA_EST_MEAN;
+  size_t off_cnt = 0, off_bits = 0;
   int words = 0;             // 64-bit bitmap words per row
   bool bitmap = false;       // rows vary in length: bitmap + scan + fill
   float scale = 0.0f;        // Top-P logit scale (resolved)
@@ -110,6 +113,8 @@ inline vsa_status select_sizes(const vsa_shape* s, const vsa_select* sel, PlanSi
   if (sel->mode != VSA_TOPK && sel->mode != VSA_TOPP) return VSA_ERR_INVALID_ARG;
   if (sel->n_value != 1 && sel->n_value != s->heads) return VSA_ERR_INVALID_ARG;
   if (sel->window_t < -1) return VSA_ERR_INVALID_ARG;
+  if (sel->estimator != VSA_EST_MEAN && sel->estimator != VSA_EST_DSA && sel->estimator != VSA_EST_DSA2)
+    return VSA_ERR_INVALID_ARG;
   if (s->heads > VSA_MAX_HEADS) return VSA_ERR_UNSUPPORTED;
   Geo g = make_geo(*s);
   if (sel->sink < 0 || sel->sink > g.NB) return VSA_ERR_INVALID_ARG;
@@ -144,10 +149,14 @@ inline vsa_status select_sizes(const vsa_shape* s, const vsa_select* sel, PlanSi
   }
   if (cap >= (int64_t(1) << 31) - 1) return VSA_ERR_UNSUPPORTED;
   out->capacity = cap;
-  size_t cent = size_t(out->rows) * s->D * sizeof(float);
-  out->off_qc = 0;
-  out->off_kc = align256(cent);
-  size_t ws = out->off_kc + align256(cent);
+  size_t cent = align256(size_t(out->rows) * s->D * sizeof(float));
+  out->estimator = sel->estimator;
+  out->n_sum = sel->estimator == VSA_EST_MEAN ? 2 : sel->estimator == VSA_EST_DSA ? 3 : 4;
+  size_t ws = 0;
+  for (int i = 0; i < out->n_sum; ++i) {
+    out->off_sum[i] = ws;
+    ws += cent;
+  }
   out->words = (g.NB + 63) / 64;
   out->bitmap = topp || sel->window_t >= 0 || sel->sink > 0;
   if (out->bitmap) {
@@ -170,6 +179,7 @@ inline vsa_status plan_sizes(const vsa_shape* s, const float* density, int n_den
   sel.window_t = window_t;
   sel.sink = 0;
   sel.scale = 0.0f;
+  sel.estimator = VSA_EST_MEAN;
   return select_sizes(s, &sel, out);
 }
 

@@ -34,17 +34,30 @@ struct SchemeArgs {
   int64_t off[VSA_MAX_SCHEMES];
 };
 
+// Block summaries an estimator reads, each float32 [BH][NB][D]: mean: qa =
+// query means, ka = key means; DSA: qa = query midpoints, ka/kb = key
+// max/min; DSA2: qa/qb = query max/min, ka/kb = key max/min.
+struct Summaries {
+  const float* qa;
+  const float* qb;
+  const float* ka;
+  const float* kb;
+};
+
 // Block means of x0 into out0 and, when x1 is not null, of x1 into out1.
 hipError_t launch_pool(const void* x0, float* out0, const void* x1, float* out1, int dtype, int D,
                        const DGeo& g, int BH, hipStream_t st);
-hipError_t launch_score_select(const float* qc, const float* kc, const DGeo& g, int D, int heads,
-                               int BH, const SelectArgs& sa, int32_t* row_ptr, int32_t* col_idx,
-                               int32_t* counts, uint64_t* bits, hipStream_t st);
+// Block max/min of x0 (or, with mid0, the midpoint into max0) and of x1.
+hipError_t launch_extremes(const void* x0, float* max0, float* min0, int mid0, const void* x1, float* max1,
+                           float* min1, int mid1, int dtype, int D, const DGeo& g, int BH, hipStream_t st);
+// est: 0 mean, 1 DSA, 2 DSA2 (vsa_estimator).
+hipError_t launch_score_select(const Summaries& sm, int est, const DGeo& g, int D, int heads, int BH,
+                               const SelectArgs& sa, int32_t* row_ptr, int32_t* col_idx, int32_t* counts,
+                               uint64_t* bits, hipStream_t st);
 hipError_t launch_scan_fill(const int32_t* counts, const uint64_t* bits, int32_t* row_ptr,
                             int32_t* col_idx, int64_t R, int words, int NB, int64_t capacity,
                             hipStream_t st);
-hipError_t launch_scores(const float* qc, const float* kc, float* out, int NB, int D, int BH,
-                         hipStream_t st);
+hipError_t launch_scores(const Summaries& sm, int est, float* out, int NB, int D, int BH, hipStream_t st);
 hipError_t launch_attn(const void* q, const void* k, const void* v, void* o, int dtype, int D,
                        const int32_t* row_ptr, const int32_t* col_idx, const DGeo& g, int BH,
                        float scale, hipStream_t st);

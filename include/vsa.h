@@ -105,6 +105,22 @@ vsa_status vsa_query(const vsa_shape* shape, const float* density, int n_density
  * head's scheme). */
 typedef enum { VSA_TOPK = 0, VSA_TOPP = 1 } vsa_select_mode;
 
+/* Summarizer and inter-estimator of the planning step (SPADE 3.1, the
+ * Summarizer and Estimator Expressions of Fig. 4).  Each reduces a block's
+ * Q or K tokens to vectors in R^D and scores a (query block, key block)
+ * pair in float32, channels in order from +0 with separately rounded
+ * products (no fused multiply-add):
+ *   VSA_EST_MEAN: block means; score = <q_mean, k_mean> (MEAN-SPADE).
+ *   VSA_EST_DSA:  channel-wise max and min over the block's tokens; the
+ *     query midpoint qm = fl(fl(q_max + q_min) * 0.5); score = sum over
+ *     channels of max(qm*k_max, qm*k_min): the largest dot product of qm
+ *     with any vector of the key block's [k_min, k_max] box (DSA-SPADE).
+ *   VSA_EST_DSA2: score = sum over channels of the largest of the four
+ *     products of {q_max, q_min} with {k_max, k_min}: the largest dot
+ *     product between the query and key boxes (DSA2-SPADE).
+ * Cut-short edge blocks use their valid tokens. */
+typedef enum { VSA_EST_MEAN = 0, VSA_EST_DSA = 1, VSA_EST_DSA2 = 2 } vsa_estimator;
+
 /* Selection options of vsa_query_select / vsa_plan_select (SPADE 3.1:
  * each head's scheme has a local-window length and an inter-top value that
  * is a Top-K keep or a Top-P cumulative threshold; the attention-sink
@@ -120,7 +136,8 @@ typedef enum { VSA_TOPK = 0, VSA_TOPP = 1 } vsa_select_mode;
  * window_t: as in vsa_query.
  * sink: 0 <= sink <= NB; key blocks 0 .. sink-1 are kept by every row.
  * scale: VSA_TOPP logit scale, 0 means 1/sqrt(D); must be finite and
- *   non-negative. */
+ *   non-negative.
+ * estimator: vsa_estimator that produces the scores being selected. */
 typedef struct {
   int32_t mode;
   int32_t n_value;
@@ -128,6 +145,7 @@ typedef struct {
   int32_t window_t;
   int32_t sink;
   float scale;
+  int32_t estimator;
 } vsa_select;
 
 /* Planning (SPADE 3.3: summarizer, inter-estimator, Top-K, union with the
@@ -149,9 +167,10 @@ vsa_status vsa_plan(const void* q, const void* k, const vsa_shape* shape,
 vsa_status vsa_query_select(const vsa_shape* shape, const vsa_select* sel, int64_t* row_ptr_len,
                             int64_t* col_capacity, size_t* plan_ws);
 
-/* Planning with a selection mode and sink blocks (SPADE 3.1 and 3.3).
- * Same inputs, arithmetic and CSR output as vsa_plan, which equals
- * vsa_plan_select with VSA_TOPK, the density as value and sink 0.
+/* Planning with an estimator, a selection mode and sink blocks (SPADE 3.1
+ * and 3.3).  Same inputs and CSR output as vsa_plan, which equals
+ * vsa_plan_select with VSA_EST_MEAN, VSA_TOPK, the density as value and
+ * sink 0.
  * VSA_TOPP works in float32 on the scores of the fixed order above: the
  * row max m, weights e_j = expf((s_j - m) * scale), sums over a wave in a
  * fixed order, and the prefix cut found by a search on the score keys,
@@ -161,6 +180,14 @@ vsa_status vsa_query_select(const vsa_shape* shape, const vsa_select* sel, int64
 vsa_status vsa_plan_select(const void* q, const void* k, const vsa_shape* shape,
                            const vsa_select* sel, vsa_index* index, void* ws, size_t ws_bytes,
                            void* stream);
+
+/* Inter-block importance matrix of an estimator alone (SPADE 3.1 Fig. 4,
+ * 3.3): q, k: device [B, heads, N, D]; out: device float32
+ * [B, heads, NB, NB], out[.., i, j] = the score vsa_plan_select ranks for
+ * query block i and key block j.  ws: device workspace of at least the
+ * plan_ws that vsa_query_select reports for the same shape and estimator. */
+vsa_status vsa_estimate(const void* q, const void* k, const vsa_shape* shape, int estimator, float* out,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /* Block-sparse attention (SPADE 2.2 Eq. 2 with M = 0 on kept block pairs and
  * -inf elsewhere; 3.3 flash block-sparse attention and layout restore).

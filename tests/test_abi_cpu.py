@@ -272,3 +272,27 @@ def test_select_entry_error_paths(lib):
     assert call(cap_=cap - 1) == _lib.VSA_ERR_CAPACITY
     assert call(ws_bytes=pws - 1) == _lib.VSA_ERR_WORKSPACE
     assert call(sel=_select(_lib.VSA_TOPP, [2.0])[0]) == _lib.VSA_ERR_INVALID_ARG
+
+
+def test_estimator_workspace_and_errors(lib):
+    """Each estimator's plan workspace holds its summaries: 2, 3 or 4 arrays
+    of [B*heads*NB, D] float32; an unknown estimator is rejected."""
+    w = W.WORKLOADS["wan13b"]
+    shape = _shape(w)
+    g = O.geometry(w.grid, w.block)
+    one = 12 * g.NB * 128 * 4
+    sizes = {}
+    for est, n in ((0, 2), (1, 3), (2, 4)):
+        sel, _keep = _select(_lib.VSA_TOPK, [0.2])
+        sel.estimator = est
+        st, rl, cap, pws = _query_select(lib, shape, sel)
+        assert st == 0
+        assert pws >= n * one
+        sizes[est] = pws
+    assert sizes[0] < sizes[1] < sizes[2]
+    bad, _keep = _select(_lib.VSA_TOPK, [0.2])
+    bad.estimator = 3
+    assert _query_select(lib, shape, bad)[0] == _lib.VSA_ERR_INVALID_ARG
+    assert lib.vsa_estimate(FAKE, FAKE, ctypes.byref(shape), 3, FAKE, FAKE, 1 << 30, None) == _lib.VSA_ERR_INVALID_ARG
+    assert lib.vsa_estimate(None, FAKE, ctypes.byref(shape), 1, FAKE, FAKE, 1 << 30, None) == _lib.VSA_ERR_INVALID_ARG
+    assert lib.vsa_estimate(FAKE, FAKE, ctypes.byref(shape), 1, FAKE, FAKE, sizes[1] // 2, None) == _lib.VSA_ERR_WORKSPACE
