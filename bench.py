@@ -103,7 +103,7 @@ def cpu_baseline(inp, w, row_ptr, col_idx, sizes, step_flops, budget_s=20.0):
     g = info["geometry"]
     rng = np.random.default_rng(0)
     t_attn, f_attn, n_rows = 0.0, 0, 0
-    while t_attn < budget_s and n_rows < 4 * g.NB:
+    while t_attn < budget_s and n_rows < 12 * g.NB:
         b, h, i = int(rng.integers(0, w.B)), int(rng.integers(0, w.heads)), int(rng.integers(0, g.NB))
         r = (b * w.heads + h) * g.NB + i
         t0 = time.perf_counter()
@@ -168,6 +168,61 @@ def time_select(vsa, lib, _lib, q, k, v, o, w, mode, val, sink, stream, sizes, e
             "row_len_min_max": [int(lens.min()), int(lens.max())]}
 
 
+def time_mixed(vsa, lib, _lib, q, k, v, o, w, stream, sizes, reps=20):
+    """A mixed per-head plan on the bench shape (dense, static, dynamic heads
+    with windows; a seeded static ranking table), timed like time_select."""
+    import ctypes
+
+    import torch
+    shape = vsa._shape_of(q, w.grid, w.block)
+    nb = len(sizes)
+    pattern = [{"kind": "dense"}, {"kind": "static", "value": 0.2}, {"kind": "dynamic", "value": 0.2, "window_t": 1},
+               {"kind": "dynamic", "value": 0.1}, {"kind": "static", "value": 0.05, "window_t": 0},
+               {"kind": "dynamic", "value": 0.3}]
+    options = [pattern[h % len(pattern)] for h in range(w.heads)]
+    table = torch.from_numpy(np.random.default_rng(24).standard_normal((w.heads, nb, nb)).astype(np.float32))
+    table = table.to(q.device).contiguous()
+    rl, cap, pws = vsa.query_mixed(shape, options)
+    dev = q.device
+    row_ptr = torch.empty(rl, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(pws, 1), dtype=torch.uint8, device=dev)
+    cidx = _lib.VsaIndex(shape, 0, 0, ctypes.c_void_p(row_ptr.data_ptr()), ctypes.c_void_p(col_idx.data_ptr()), cap)
+    opts = vsa._head_options(options)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    qp, kp, vp, op, tp = (ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, o, table))
+
+    def plan_call():
+        _lib.check(lib.vsa_plan_mixed(qp, kp, ctypes.byref(shape), opts, 0, tp, ctypes.byref(cidx),
+                                      ctypes.c_void_p(ws.data_ptr()), ws.numel(), sp), "vsa_plan_mixed")
+
+    def attn_call():
+        _lib.check(lib.vsa_attn(qp, kp, vp, ctypes.byref(cidx), ctypes.c_float(0.0), op, None, 0, sp), "vsa_attn")
+
+    for _ in range(2):
+        plan_call(); attn_call()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record(stream)
+    for _ in range(reps):
+        plan_call()
+    e[1].record(stream)
+    for _ in range(reps // 2):
+        attn_call()
+    e[2].record(stream)
+    torch.cuda.synchronize()
+    plan_ms = e[0].elapsed_time(e[1]) / reps
+    attn_ms = e[1].elapsed_time(e[2]) / (reps // 2)
+    rp = row_ptr.cpu().numpy().astype(np.int64)
+    ci = col_idx.cpu().numpy().astype(np.int64)[: int(rp[-1])]
+    flops = executed_flops(rp, ci, sizes, w.D)
+    return {"heads": [o["kind"] + (f" {o['value']}" if "value" in o else "") +
+                      (f" w{o['window_t']}" if o.get("window_t", -1) >= 0 else "") for o in options],
+            "plan_ms": round(plan_ms, 4), "attn_ms": round(attn_ms, 4),
+            "attn_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 2),
+            "nnz_blocks": int(rp[-1]), "density": round(float(rp[-1]) / ((len(rp) - 1) * nb), 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -175,6 +230,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan13b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the scheme-selection, selection-variant and mixed-plan timings "
+                         "(profiled runs: only the step's own launches)")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run one plain device-to-device copy of MIB MiB (HBM counter scale)")
@@ -306,7 +364,7 @@ def main():
     # Scheme generation (outside the timed step): head-wise blocking-scheme
     # selection over three 128-token candidates; it reads Q and K once per
     # candidate, so it is reported against the HBM roofline.
-    if w.dtype == "bf16" and w.D == 128 and w.name == "wan13b":
+    if w.dtype == "bf16" and w.D == 128 and w.name == "wan13b" and not a.no_extras:
         cands = [(4, 4, 8), (1, 8, 16), (2, 8, 8)]
         for _ in range(3):
             vsa.select_scheme(q, k, w.grid, cands)
@@ -327,11 +385,12 @@ def main():
     # Selection variants (outside the timed step): Top-P and Top-K with
     # attention-sink blocks, each planned in place into preallocated buffers
     # and followed by attention over the index it produced.
-    if w.dtype == "bf16" and w.name == "wan13b":
+    if w.dtype == "bf16" and w.name == "wan13b" and not a.no_extras:
         result["select_variants"] = [
             time_select(vsa, lib, _lib, q, k, v, o, w, mode, val, sink, stream, sizes, est)
             for est, mode, val, sink in (("mean", "topp", 0.25, 2), ("mean", "topk", 0.2, 2),
                                          ("dsa", "topk", 0.2, 0), ("dsa2", "topk", 0.2, 0))]
+        result["mixed_plan"] = time_mixed(vsa, lib, _lib, q, k, v, o, w, stream, sizes)
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inp, w, rp, ci, sizes, flops, a.cpu_budget)

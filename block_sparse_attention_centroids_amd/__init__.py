@@ -21,9 +21,9 @@ from typing import Optional, Sequence, Tuple, Union
 import torch
 
 from . import _lib
-from ._lib import VsaError, VsaIndex, VsaSelect, VsaShape, check, load
+from ._lib import VsaError, VsaHeadOption, VsaIndex, VsaSelect, VsaShape, check, load
 
-__all__ = ["plan", "plan_select", "attn", "query", "query_select", "permute", "unpermute",
+__all__ = ["plan", "plan_select", "plan_mixed", "attn", "query", "query_select", "permute", "unpermute",
            "centroids", "centroid_scores", "estimate", "sics", "select_scheme", "Index", "VsaError", "load"]
 
 _DTYPES = {torch.bfloat16: _lib.VSA_BF16, torch.float32: _lib.VSA_F32}
@@ -67,10 +67,11 @@ class Index:
     row_ptr: torch.Tensor
     col_idx: torch.Tensor
     capacity: int
+    equal_heads: int = 0
 
     def c_index(self) -> VsaIndex:
         return VsaIndex(self.shape, self.nb, self.window_t, ctypes.c_void_p(self.row_ptr.data_ptr()),
-                        ctypes.c_void_p(self.col_idx.data_ptr()), self.capacity)
+                        ctypes.c_void_p(self.col_idx.data_ptr()), self.capacity, self.equal_heads)
 
     @property
     def grid(self) -> Tuple[int, int, int]:
@@ -113,7 +114,7 @@ def plan(q: torch.Tensor, k: torch.Tensor, grid, block, density: Union[float, Se
     check(lib.vsa_plan(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
                        ctypes.byref(shape), dens, nd, int(window_t), ctypes.byref(cidx),
                        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(q)), "vsa_plan")
-    return Index(cidx.shape, cidx.nb, cidx.window_t, row_ptr, col_idx, cap)
+    return Index(cidx.shape, cidx.nb, cidx.window_t, row_ptr, col_idx, cap, cidx.equal_heads)
 
 
 _MODES = {"topk": _lib.VSA_TOPK, "topp": _lib.VSA_TOPP}
@@ -169,7 +170,66 @@ def plan_select(q: torch.Tensor, k: torch.Tensor, grid, block, mode: str,
     check(lib.vsa_plan_select(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
                               ctypes.byref(shape), ctypes.byref(sel), ctypes.byref(cidx),
                               ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(q)), "vsa_plan_select")
-    return Index(cidx.shape, cidx.nb, cidx.window_t, row_ptr, col_idx, cap)
+    return Index(cidx.shape, cidx.nb, cidx.window_t, row_ptr, col_idx, cap, cidx.equal_heads)
+
+
+_KINDS = {"dynamic": _lib.VSA_HEAD_DYNAMIC, "static": _lib.VSA_HEAD_STATIC, "dense": _lib.VSA_HEAD_DENSE}
+
+
+def _head_options(options):
+    arr = (VsaHeadOption * len(options))()
+    for h, o in enumerate(options):
+        if o["kind"] not in _KINDS:
+            raise ValueError(f"head kind must be one of {sorted(_KINDS)}")
+        arr[h] = VsaHeadOption(_KINDS[o["kind"]], float(o.get("value", 1.0)), int(o.get("window_t", -1)))
+    return arr
+
+
+def query_mixed(shape: VsaShape, options, estimator: str = "mean"):
+    """(row_ptr_len, col_capacity, plan_ws_bytes) for plan_mixed."""
+    lib = load()
+    opts = _head_options(options)
+    rl, cap, pws = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
+    check(lib.vsa_query_mixed(ctypes.byref(shape), opts, _estimator(estimator), ctypes.byref(rl),
+                              ctypes.byref(cap), ctypes.byref(pws)), "vsa_query_mixed")
+    return rl.value, cap.value, pws.value
+
+
+def plan_mixed(q: Optional[torch.Tensor], k: Optional[torch.Tensor], grid, block, options,
+               static_scores: Optional[torch.Tensor] = None, estimator: str = "mean",
+               B: Optional[int] = None, D: Optional[int] = None, dtype=torch.bfloat16,
+               device=None) -> Index:
+    """Mixed per-head plan.  options: one dict per head, {"kind": "dynamic" |
+    "static" | "dense", "value": keep rate, "window_t": r}.  static_scores:
+    float32 [heads, NB, NB] on the device for static heads.  q and k may be
+    None when no head is dynamic; then B, D, dtype and device describe the
+    index (it depends on the table alone and can be reused)."""
+    lib = load()
+    if q is not None:
+        shape = _shape_of(q, grid, block)
+        if k is None or k.shape != q.shape or k.dtype != q.dtype or not k.is_contiguous():
+            raise ValueError("k must match q")
+        dev = q.device
+    else:
+        T, H, W = (int(a) for a in grid)
+        shape = VsaShape(int(B), len(options), int(D), T, H, W, *(int(a) for a in block), _DTYPES[dtype])
+        dev = torch.device(device) if device is not None else static_scores.device
+    if len(options) != shape.heads:
+        raise ValueError("one option per head")
+    if static_scores is not None and (static_scores.dtype != torch.float32 or not static_scores.is_contiguous()):
+        raise ValueError("static_scores must be contiguous float32 [heads, NB, NB]")
+    rl, cap, pws = query_mixed(shape, options, estimator)
+    row_ptr = torch.empty(rl, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(pws, 1), dtype=torch.uint8, device=dev)
+    cidx = VsaIndex(shape, 0, 0, ctypes.c_void_p(row_ptr.data_ptr()), ctypes.c_void_p(col_idx.data_ptr()), cap)
+    opts = _head_options(options)
+    ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    check(lib.vsa_plan_mixed(ptr(q), ptr(k), ctypes.byref(shape), opts, _estimator(estimator), ptr(static_scores),
+                             ctypes.byref(cidx), ctypes.c_void_p(ws.data_ptr()), ws.numel(), stream),
+          "vsa_plan_mixed")
+    return Index(cidx.shape, cidx.nb, cidx.window_t, row_ptr, col_idx, cap, cidx.equal_heads)
 
 
 def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: Index,

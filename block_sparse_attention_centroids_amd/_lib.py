@@ -25,6 +25,10 @@ VSA_EST_MEAN = 0
 VSA_EST_DSA = 1
 VSA_EST_DSA2 = 2
 
+VSA_HEAD_DYNAMIC = 0
+VSA_HEAD_STATIC = 1
+VSA_HEAD_DENSE = 2
+
 
 class VsaShape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("heads", ctypes.c_int32), ("D", ctypes.c_int32),
@@ -36,13 +40,17 @@ class VsaShape(ctypes.Structure):
 class VsaIndex(ctypes.Structure):
     _fields_ = [("shape", VsaShape), ("nb", ctypes.c_int32), ("window_t", ctypes.c_int32),
                 ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p),
-                ("capacity", ctypes.c_int64)]
+                ("capacity", ctypes.c_int64), ("equal_heads", ctypes.c_int32)]
 
 
 class VsaSelect(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("n_value", ctypes.c_int32),
                 ("value", ctypes.POINTER(ctypes.c_float)), ("window_t", ctypes.c_int32),
                 ("sink", ctypes.c_int32), ("scale", ctypes.c_float), ("estimator", ctypes.c_int32)]
+
+
+class VsaHeadOption(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("value", ctypes.c_float), ("window_t", ctypes.c_int32)]
 
 
 class VsaError(RuntimeError):
@@ -55,7 +63,8 @@ _lib = None
 
 EXPORTS = ("vsa_query", "vsa_plan", "vsa_attn", "vsa_permute", "vsa_unpermute",
            "vsa_centroids", "vsa_centroid_scores", "vsa_sics", "vsa_scheme_workspace",
-           "vsa_select_scheme", "vsa_query_select", "vsa_plan_select", "vsa_estimate", "vsa_status_str")
+           "vsa_select_scheme", "vsa_query_select", "vsa_plan_select", "vsa_estimate", "vsa_query_mixed", "vsa_plan_mixed",
+           "vsa_status_str")
 
 
 def load() -> ctypes.CDLL:
@@ -92,6 +101,11 @@ def load() -> ctypes.CDLL:
     lib.vsa_plan_select.argtypes = [P, P, ctypes.POINTER(VsaShape), ctypes.POINTER(VsaSelect),
                                     ctypes.POINTER(VsaIndex), P, ctypes.c_size_t, P]
     lib.vsa_estimate.argtypes = [P, P, ctypes.POINTER(VsaShape), I, P, P, ctypes.c_size_t, P]
+    lib.vsa_query_mixed.argtypes = [ctypes.POINTER(VsaShape), ctypes.POINTER(VsaHeadOption), I,
+                                    ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                                    ctypes.POINTER(ctypes.c_size_t)]
+    lib.vsa_plan_mixed.argtypes = [P, P, ctypes.POINTER(VsaShape), ctypes.POINTER(VsaHeadOption), I, P,
+                                   ctypes.POINTER(VsaIndex), P, ctypes.c_size_t, P]
     for name in EXPORTS[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     lib.vsa_status_str.argtypes = [ctypes.c_int]

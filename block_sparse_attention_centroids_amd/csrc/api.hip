@@ -109,6 +109,69 @@ vsa_status vsa_query_select(const vsa_shape* shape, const vsa_select* sel, int64
   }
 }
 
+}  // extern "C"
+
+namespace {
+
+// Enqueue a plan whose sizes and per-head parameters are in ps: summaries
+// (when a head is dynamic), scoring + selection, then scan + fill when rows
+// vary in length.  Everything the host can check has been checked.
+vsa_status run_plan(const void* q, const void* k, const vsa_shape* shape, const PlanSizes& ps, int topp,
+                    int sink, const float* table, vsa_index* index, void* ws, void* stream) {
+  const Geo g = make_geo(*shape);
+  const DGeo dg = to_dgeo(g);
+  const int BH = shape->B * shape->heads;
+  hipStream_t st_ = reinterpret_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+
+  SelectArgs sa;
+  std::memset(&sa, 0, sizeof(sa));
+  int64_t sumk = 0;
+  for (int h = 0; h < shape->heads; ++h) {
+    if (topp) {
+      sa.p[h] = ps.p[h];
+    } else {
+      sa.k[h] = ps.k[h];
+      sa.off[h] = static_cast<int32_t>(sumk);
+      sumk += ps.k[h];
+    }
+    sa.win[h] = static_cast<int16_t>(ps.win[h]);
+    sa.kind[h] = static_cast<int8_t>(ps.kind[h]);
+  }
+  sa.batch_stride = sumk * g.NB;
+  sa.rows = ps.rows;
+  sa.table = table;
+  sa.words = ps.words;
+  sa.sink = sink;
+  sa.bitmap = ps.bitmap ? 1 : 0;
+  sa.scale = ps.scale;
+  sa.topp = topp;
+  int32_t* counts = ps.bitmap ? reinterpret_cast<int32_t*>(w + ps.off_cnt) : nullptr;
+  uint64_t* bits = ps.bitmap ? reinterpret_cast<uint64_t*>(w + ps.off_bits) : nullptr;
+
+  index->shape = *shape;
+  index->nb = g.NB;
+  index->window_t = ps.max_win;
+  index->equal_heads = 1;
+  for (int h = 0; h < shape->heads; ++h)
+    if (topp || ps.k[h] != ps.k[0] || ps.win[h] != ps.win[0]) index->equal_heads = 0;
+
+  Summaries sm{nullptr, nullptr, nullptr, nullptr};
+  hipError_t e = hipSuccess;
+  if (ps.any_dynamic) e = summarize(q, k, shape, ps, w, dg, BH, st_, &sm);
+  if (e == hipSuccess)
+    e = launch_score_select(sm, ps.estimator, dg, shape->D, shape->heads, BH, sa, index->row_ptr,
+                            index->col_idx, counts, bits, st_);
+  if (e == hipSuccess && ps.bitmap)
+    e = launch_scan_fill(counts, bits, index->row_ptr, index->col_idx, ps.rows, ps.words, g.NB,
+                         index->capacity, st_);
+  return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
 vsa_status vsa_plan_select(const void* q, const void* k, const vsa_shape* shape, const vsa_select* sel,
                            vsa_index* index, void* ws, size_t ws_bytes, void* stream) {
   try {
@@ -120,49 +183,42 @@ vsa_status vsa_plan_select(const void* q, const void* k, const vsa_shape* shape,
     if (!aligned16(q) || !aligned16(k) || !aligned16(ws)) return VSA_ERR_INVALID_ARG;
     if (index->capacity < ps.capacity) return VSA_ERR_CAPACITY;
     if (ws_bytes < ps.ws) return VSA_ERR_WORKSPACE;
-    const Geo g = make_geo(*shape);
-    const DGeo dg = to_dgeo(g);
-    const int BH = shape->B * shape->heads;
-    hipStream_t st_ = reinterpret_cast<hipStream_t>(stream);
-    char* w = static_cast<char*>(ws);
+    return run_plan(q, k, shape, ps, sel->mode == VSA_TOPP ? 1 : 0, sel->sink, nullptr, index, ws, stream);
+  } catch (...) {
+    return VSA_ERR_INVALID_ARG;
+  }
+}
 
-    SelectArgs sa;
-    std::memset(&sa, 0, sizeof(sa));
-    const bool topp = sel->mode == VSA_TOPP;
-    int64_t sumk = 0;
-    for (int h = 0; h < shape->heads; ++h) {
-      if (topp) {
-        sa.p[h] = ps.p[h];
-      } else {
-        sa.k[h] = ps.k[h];
-        sa.off[h] = static_cast<int32_t>(sumk);
-        sumk += ps.k[h];
-      }
-    }
-    sa.batch_stride = sumk * g.NB;
-    sa.rows = ps.rows;
-    sa.window_t = sel->window_t;
-    sa.words = ps.words;
-    sa.sink = sel->sink;
-    sa.bitmap = ps.bitmap ? 1 : 0;
-    sa.scale = ps.scale;
-    sa.topp = topp ? 1 : 0;
-    int32_t* counts = ps.bitmap ? reinterpret_cast<int32_t*>(w + ps.off_cnt) : nullptr;
-    uint64_t* bits = ps.bitmap ? reinterpret_cast<uint64_t*>(w + ps.off_bits) : nullptr;
+vsa_status vsa_query_mixed(const vsa_shape* shape, const vsa_head_option* options, int estimator,
+                           int64_t* row_ptr_len, int64_t* col_capacity, size_t* plan_ws) {
+  try {
+    PlanSizes ps;
+    vsa_status st = mixed_sizes(shape, options, estimator, &ps);
+    if (st != VSA_OK) return st;
+    if (row_ptr_len) *row_ptr_len = ps.rows + 1;
+    if (col_capacity) *col_capacity = ps.capacity;
+    if (plan_ws) *plan_ws = ps.ws;
+    return VSA_OK;
+  } catch (...) {
+    return VSA_ERR_INVALID_ARG;
+  }
+}
 
-    index->shape = *shape;
-    index->nb = g.NB;
-    index->window_t = sel->window_t;
-
-    Summaries sm;
-    hipError_t e = summarize(q, k, shape, ps, w, dg, BH, st_, &sm);
-    if (e == hipSuccess)
-      e = launch_score_select(sm, ps.estimator, dg, shape->D, shape->heads, BH, sa, index->row_ptr,
-                              index->col_idx, counts, bits, st_);
-    if (e == hipSuccess && ps.bitmap)
-      e = launch_scan_fill(counts, bits, index->row_ptr, index->col_idx, ps.rows, ps.words, g.NB,
-                           index->capacity, st_);
-    return hip_status(e);
+vsa_status vsa_plan_mixed(const void* q, const void* k, const vsa_shape* shape,
+                          const vsa_head_option* options, int estimator, const float* static_scores,
+                          vsa_index* index, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    if (!index) return VSA_ERR_INVALID_ARG;
+    PlanSizes ps;
+    vsa_status st = mixed_sizes(shape, options, estimator, &ps);
+    if (st != VSA_OK) return st;
+    if (!index->row_ptr || !index->col_idx) return VSA_ERR_INVALID_ARG;
+    if (ps.any_dynamic && (!q || !k || !aligned16(q) || !aligned16(k))) return VSA_ERR_INVALID_ARG;
+    if (ps.any_static && !static_scores) return VSA_ERR_INVALID_ARG;
+    if (ps.ws > 0 && (!ws || !aligned16(ws))) return VSA_ERR_INVALID_ARG;
+    if (index->capacity < ps.capacity) return VSA_ERR_CAPACITY;
+    if (ws_bytes < ps.ws) return VSA_ERR_WORKSPACE;
+    return run_plan(q, k, shape, ps, 0, 0, static_scores, index, ws, stream);
   } catch (...) {
     return VSA_ERR_INVALID_ARG;
   }
@@ -229,7 +285,7 @@ vsa_status vsa_attn(const void* q, const void* k, const void* v, const vsa_index
   if (!(scale > 0.0f) || !std::isfinite(scale)) return VSA_ERR_INVALID_ARG;
   const int BH = index->shape.B * index->shape.heads;
   hipError_t e = launch_attn(q, k, v, o, index->shape.dtype, index->shape.D, index->row_ptr,
-                             index->col_idx, to_dgeo(g), BH, scale,
+                             index->col_idx, to_dgeo(g), BH, scale, index->equal_heads != 0,
                              reinterpret_cast<hipStream_t>(stream));
   return hip_status(e);
 }

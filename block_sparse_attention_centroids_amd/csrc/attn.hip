@@ -185,7 +185,7 @@ template <int D>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
-    DGeo g, float scale_log2) {
+    DGeo g, float scale_log2, int contiguous) {
   using C = AttnCfg<D>;
   constexpr int PARTS = C::PARTS, IPW = C::IPW, ROW = C::ROW, TILE = C::TILE;
   constexpr int RPI = C::ROWS_PER_INST;
@@ -217,15 +217,42 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   }
 
-  // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
-  // contiguous range of (head, query block) items so that neighbouring
-  // query blocks of a head, which keep overlapping key blocks, share an L2.
+  // Workgroups are dealt round-robin to the 8 XCDs, and an XCD runs its
+  // workgroups in order.  Neighbouring query blocks of a head keep
+  // overlapping key blocks, so each XCD gets contiguous query blocks to
+  // share its L2:
+  //  * heads of equal work: one contiguous run of (head, query block) rows;
+  //  * otherwise an equal contiguous slice of every head, head after head,
+  //    so a heavy head (dense, or a high keep rate) is spread over all XCDs.
+  //    Head h's NB = 8a + bx rows give a or a + 1 to each XCD; the bx extra
+  //    rows of head h go to XCDs (h*bx + t) mod 8, t < bx, which matches the
+  //    hardware's deal of BH*NB workgroups exactly.
   const int nwg = gridDim.x;
   const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
-  const int per = (nwg + 7) >> 3, rem = nwg & 7;
-  const int logical = (rem == 0 || xcd < rem) ? xcd * per + loc : rem * per + (xcd - rem) * (per - 1) + loc;
-
-  const int bh = logical / g.NB, i = logical - bh * g.NB;
+  int bh, i;
+  if (contiguous) {
+    const int per = (nwg + 7) >> 3, rem = nwg & 7;
+    const int logical = (rem == 0 || xcd < rem) ? xcd * per + loc : rem * per + (xcd - rem) * (per - 1) + loc;
+    bh = logical / g.NB;
+    i = logical - bh * g.NB;
+  } else {
+    const int NB = g.NB, BHn = nwg / NB;
+    const int a = NB >> 3, bx = NB & 7;
+    // Rows XCD xcd receives from heads 0 .. h-1.
+    auto prefix = [&](int h) {
+      const int t = h * bx - xcd;
+      return a * h + (t > 0 ? (t + 7) >> 3 : 0);
+    };
+    int h = min((int)(((long long)loc * 8) / NB), BHn - 1);
+    while (h > 0 && prefix(h) > loc) --h;
+    while (h + 1 < BHn && prefix(h + 1) <= loc) ++h;
+    int start = a * xcd;
+    for (int x2 = 0; x2 < xcd; ++x2) start += (((x2 - h * bx) % 8 + 8) % 8) < bx ? 1 : 0;
+    bh = h;
+    i = start + loc - prefix(h);
+  }
+  bh = uniform(bh);
+  i = uniform(i);
   const Box bi = block_box(g, i);
   const int ni = bi.n();
   TokenMap qmap;
@@ -604,16 +631,17 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
 
 hipError_t launch_attn(const void* q, const void* k, const void* v, void* o, int dtype, int D,
                        const int32_t* row_ptr, const int32_t* col_idx, const DGeo& g, int BH,
-                       float scale, hipStream_t st) {
+                       float scale, bool contiguous, hipStream_t st) {
   const unsigned nwg = (unsigned)BH * (unsigned)g.NB;
   if (dtype == VSA_BF16) {
     const float sl2 = scale * 1.4426950408889634f;
+    const int cont = contiguous ? 1 : 0;
     if (D == 128)
       hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(nwg), dim3(THREADS), 0, st, (const uint16_t*)q,
-                         (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, row_ptr, col_idx, g, sl2);
+                         (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, row_ptr, col_idx, g, sl2, cont);
     else
       hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(nwg), dim3(THREADS), 0, st, (const uint16_t*)q,
-                         (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, row_ptr, col_idx, g, sl2);
+                         (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, row_ptr, col_idx, g, sl2, cont);
   } else {
     if (D == 128)
       hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(nwg), dim3(128), 0, st, (const float*)q,

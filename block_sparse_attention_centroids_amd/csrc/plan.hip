@@ -456,12 +456,24 @@ __global__ __launch_bounds__(256) void score_select_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int rows_here = min(RT, NB - i0);
   // Phase 1: scores.  Rows past NB reuse the last valid row (never emitted).
+  // A static head reads its scores from the caller's table; a dense head
+  // keeps every block, so its keys are all equal.
+  const int h = bh % heads;
+  const int b = bh / heads;
+  const int kind = sa.kind[h];
   const size_t head = (size_t)bh * NB * D;
   const float* qa = sm.qa + head;
   const float* qb = EST == 2 ? sm.qb + head : nullptr;
   const float* ka = sm.ka + head;
   const float* kb = EST != 0 ? sm.kb + head : nullptr;
-  if (rows_here == RT) {
+  if (kind == 1) {
+    const float* tab = sa.table + ((size_t)h * NB + i0) * NB;
+    for (int r = 0; r < rows_here; ++r)
+      for (int j = tid; j < NB; j += 256) smem[r * NB + j] = order_key(tab[(size_t)r * NB + j]);
+  } else if (kind == 2) {
+    for (int r = 0; r < rows_here; ++r)
+      for (int j = tid; j < NB; j += 256) smem[r * NB + j] = 0x80000000u;
+  } else if (rows_here == RT) {
     for (int j = tid; j < NB; j += 256) {
       float acc[RT];
       est_column<EST, RT>(qa + (size_t)i0 * D, qb + (EST == 2 ? (size_t)i0 * D : 0), ka + (size_t)j * D,
@@ -483,9 +495,8 @@ __global__ __launch_bounds__(256) void score_select_kernel(
   __syncthreads();
 
   // Phase 2: selection, one wave per row.
-  const int h = bh % heads;
-  const int b = bh / heads;
   const int kk = TOPP ? 0 : sa.k[h];
+  const int win = sa.win[h];
   const int per_t = g.nbh * g.nbw;
   for (int r = wave; r < rows_here; r += 4) {
     const int i = i0 + r;
@@ -515,7 +526,7 @@ __global__ __launch_bounds__(256) void score_select_kernel(
       bool keep = valid && (key > thr || (eq && rank_eq < need));
       if (sa.bitmap && valid) {
         const int dt = j / per_t - tbi;
-        keep = keep || (sa.window_t >= 0 && dt <= sa.window_t && -dt <= sa.window_t) || j < sa.sink;
+        keep = keep || (win >= 0 && dt <= win && -dt <= win) || j < sa.sink;
       }
       const uint64_t km = __ballot(keep);
       if (sa.bitmap) {

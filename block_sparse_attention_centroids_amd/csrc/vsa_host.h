@@ -102,7 +102,33 @@ struct PlanSizes {
   float scale = 0.0f;        // Top-P logit scale (resolved)
   std::vector<int> k;        // per head (Top-K)
   std::vector<float> p;      // per head (Top-P)
+  std::vector<int> win;      // per head temporal window (-1: none)
+  std::vector<int> kind;     // per head option (vsa_head_kind)
+  bool any_dynamic = true;   // some head needs Q/K summaries
+  bool any_static = false;   // some head reads the static score table
+  int max_win = -1;
 };
+
+// Summary workspace regions for an estimator, then the bitmap regions when
+// rows vary in length; sets off_sum, n_sum, off_cnt, off_bits, ws.
+inline void layout_workspace(const vsa_shape* s, PlanSizes* out) {
+  size_t cent = align256(size_t(out->rows) * s->D * sizeof(float));
+  out->n_sum = out->estimator == VSA_EST_MEAN ? 2 : out->estimator == VSA_EST_DSA ? 3 : 4;
+  size_t ws = 0;
+  if (out->any_dynamic) {
+    for (int i = 0; i < out->n_sum; ++i) {
+      out->off_sum[i] = ws;
+      ws += cent;
+    }
+  }
+  if (out->bitmap) {
+    out->off_cnt = ws;
+    ws += align256(size_t(out->rows + 1) * sizeof(int32_t));
+    out->off_bits = ws;
+    ws += align256(size_t(out->rows) * out->words * sizeof(uint64_t));
+  }
+  out->ws = ws;
+}
 
 // Sizes and per-head parameters of a selection; validates everything the
 // host can see.
@@ -149,23 +175,69 @@ inline vsa_status select_sizes(const vsa_shape* s, const vsa_select* sel, PlanSi
   }
   if (cap >= (int64_t(1) << 31) - 1) return VSA_ERR_UNSUPPORTED;
   out->capacity = cap;
-  size_t cent = align256(size_t(out->rows) * s->D * sizeof(float));
   out->estimator = sel->estimator;
-  out->n_sum = sel->estimator == VSA_EST_MEAN ? 2 : sel->estimator == VSA_EST_DSA ? 3 : 4;
-  size_t ws = 0;
-  for (int i = 0; i < out->n_sum; ++i) {
-    out->off_sum[i] = ws;
-    ws += cent;
-  }
+  out->win.assign(s->heads, sel->window_t);
+  out->kind.assign(s->heads, VSA_HEAD_DYNAMIC);
+  out->any_dynamic = true;
+  out->any_static = false;
+  out->max_win = sel->window_t;
   out->words = (g.NB + 63) / 64;
   out->bitmap = topp || sel->window_t >= 0 || sel->sink > 0;
-  if (out->bitmap) {
-    out->off_cnt = ws;
-    ws += align256(size_t(out->rows + 1) * sizeof(int32_t));
-    out->off_bits = ws;
-    ws += align256(size_t(out->rows) * out->words * sizeof(uint64_t));
+  layout_workspace(s, out);
+  return VSA_OK;
+}
+
+// Mixed per-head plans: each head is dynamic (Top-K at value over the
+// estimator's scores), static (Top-K at value over a caller table) or dense,
+// with its own window.
+inline vsa_status mixed_sizes(const vsa_shape* s, const vsa_head_option* opts, int estimator,
+                              PlanSizes* out) {
+  vsa_status st = check_shape(s);
+  if (st != VSA_OK) return st;
+  if (!opts || !out) return VSA_ERR_INVALID_ARG;
+  if (estimator != VSA_EST_MEAN && estimator != VSA_EST_DSA && estimator != VSA_EST_DSA2)
+    return VSA_ERR_INVALID_ARG;
+  if (s->heads > VSA_MAX_HEADS) return VSA_ERR_UNSUPPORTED;
+  Geo g = make_geo(*s);
+  out->k.assign(s->heads, 0);
+  out->p.assign(s->heads, 0.0f);
+  out->win.assign(s->heads, -1);
+  out->kind.assign(s->heads, VSA_HEAD_DYNAMIC);
+  out->any_dynamic = out->any_static = false;
+  out->max_win = -1;
+  for (int h = 0; h < s->heads; ++h) {
+    const vsa_head_option& o = opts[h];
+    if (o.kind != VSA_HEAD_DYNAMIC && o.kind != VSA_HEAD_STATIC && o.kind != VSA_HEAD_DENSE)
+      return VSA_ERR_INVALID_ARG;
+    if (o.window_t < -1 || o.window_t > 32767) return VSA_ERR_INVALID_ARG;
+    if (o.kind == VSA_HEAD_DENSE) {
+      out->k[h] = g.NB;
+    } else {
+      if (!(o.value > 0.0f) || !(o.value <= 1.0f)) return VSA_ERR_INVALID_ARG;
+      out->k[h] = k_rule(o.value, g.NB);
+    }
+    out->kind[h] = o.kind;
+    out->win[h] = o.window_t;
+    out->any_dynamic = out->any_dynamic || o.kind == VSA_HEAD_DYNAMIC;
+    out->any_static = out->any_static || o.kind == VSA_HEAD_STATIC;
+    out->max_win = std::max(out->max_win, o.window_t);
   }
-  out->ws = ws;
+  out->estimator = estimator;
+  out->scale = 1.0f;
+  out->rows = int64_t(s->B) * s->heads * g.NB;
+  int64_t cap = 0;
+  for (int h = 0; h < s->heads; ++h) {
+    for (int i = 0; i < g.NB; ++i) {
+      int tb = i / (g.nbh * g.nbw);
+      cap += std::min<int64_t>(int64_t(out->k[h]) + window_count(g, tb, out->win[h]), g.NB);
+    }
+  }
+  cap *= s->B;
+  if (cap >= (int64_t(1) << 31) - 1) return VSA_ERR_UNSUPPORTED;
+  out->capacity = cap;
+  out->words = (g.NB + 63) / 64;
+  out->bitmap = out->max_win >= 0;
+  layout_workspace(s, out);
   return VSA_OK;
 }
 

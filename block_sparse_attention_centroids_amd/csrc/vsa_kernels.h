@@ -18,7 +18,9 @@ struct SelectArgs {
   int32_t off[VSA_MAX_HEADS];   // Top-K: sum of k over heads before h
   int64_t batch_stride;         // Top-K: NB * sum_h k_h, col_idx entries per batch item
   int64_t rows;                 // B * heads * NB
-  int32_t window_t;             // -1: none
+  const float* table;           // static heads: scores [heads][NB][NB]
+  int16_t win[VSA_MAX_HEADS];   // temporal window of head h, -1: none
+  int8_t kind[VSA_MAX_HEADS];   // head option: 0 dynamic, 1 static, 2 dense
   int32_t words;                // 64-bit bitmap words per row
   int32_t sink;                 // key blocks 0 .. sink-1 kept by every row
   int32_t bitmap;               // rows vary: write bitmaps and counts for scan + fill
@@ -58,9 +60,11 @@ hipError_t launch_scan_fill(const int32_t* counts, const uint64_t* bits, int32_t
                             int32_t* col_idx, int64_t R, int words, int NB, int64_t capacity,
                             hipStream_t st);
 hipError_t launch_scores(const Summaries& sm, int est, float* out, int NB, int D, int BH, hipStream_t st);
+// contiguous: give each XCD one contiguous run of rows (heads of equal
+// work); otherwise an equal contiguous slice of every head.
 hipError_t launch_attn(const void* q, const void* k, const void* v, void* o, int dtype, int D,
                        const int32_t* row_ptr, const int32_t* col_idx, const DGeo& g, int BH,
-                       float scale, hipStream_t st);
+                       float scale, bool contiguous, hipStream_t st);
 // Per-block SICS of x0 into out0 and, when x1 is not null, of x1 into out1.
 hipError_t launch_sics(const void* x0, float* out0, const void* x1, float* out1, int dtype, int D,
                        const DGeo& g, int BH, hipStream_t st);

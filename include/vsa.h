@@ -72,8 +72,15 @@ typedef struct {
  * blocks kept by query block i of head (b, h) in ascending id order:
  * col_idx[row_ptr[r] .. row_ptr[r+1]).  row_ptr[0] = 0.
  * row_ptr: device int32[B*heads*nb + 1]; col_idx: device int32[capacity].
- * The caller owns both arrays; vsa_plan fills them and sets shape, nb and
- * window_t. */
+ * The caller owns both arrays; vsa_plan fills them and sets shape, nb,
+ * window_t and equal_heads.
+ * equal_heads: a scheduling hint.  The planners set 1 when every (batch,
+ * head) has the same selection size and window by construction (Top-K with
+ * one k and one window for all heads), else 0.  vsa_attn then gives each
+ * XCD a contiguous run of (head, query block) rows; with 0 it gives each
+ * XCD an equal contiguous slice of every head, which balances heads of
+ * different work.  Either value gives the same result; 0 is the safe
+ * choice for an index built by hand. */
 typedef struct {
   vsa_shape shape;
   int32_t nb;
@@ -81,6 +88,7 @@ typedef struct {
   int32_t* row_ptr;
   int32_t* col_idx;
   int64_t capacity;
+  int32_t equal_heads;
 } vsa_index;
 
 /* Largest supported head count with per-head densities, and block size. */
@@ -180,6 +188,47 @@ vsa_status vsa_query_select(const vsa_shape* shape, const vsa_select* sel, int64
 vsa_status vsa_plan_select(const void* q, const void* k, const vsa_shape* shape,
                            const vsa_select* sel, vsa_index* index, void* ws, size_t ws_bytes,
                            void* stream);
+
+/* Option of one head in a mixed plan (DecoupAttn Plans, introduction: a
+ * compiled plan gives each (timestep, layer, head) unit one option -- dense
+ * or static at a keep rate theta chosen from an offline block ranking --
+ * next to the dynamic estimator; SPADE 3.1: each head's scheme has its own
+ * local-window length and Top-K keep). */
+typedef enum { VSA_HEAD_DYNAMIC = 0, VSA_HEAD_STATIC = 1, VSA_HEAD_DENSE = 2 } vsa_head_kind;
+
+/* kind: vsa_head_kind.
+ * value: keep rate in (0, 1] for VSA_HEAD_DYNAMIC (over the estimator's
+ *   scores of this call's Q and K) and VSA_HEAD_STATIC (over the caller's
+ *   static score table); k as in vsa_query.  Ignored for VSA_HEAD_DENSE,
+ *   which keeps every key block.
+ * window_t: -1 or 0 <= r <= 32767, this head's temporal window as in
+ *   vsa_query. */
+typedef struct {
+  int32_t kind;
+  float value;
+  int32_t window_t;
+} vsa_head_option;
+
+/* Host-only sizing of a mixed plan.  options: host [heads]; estimator:
+ * vsa_estimator of the dynamic heads.  col_capacity = sum over rows of
+ * min(NB, k_h + window blocks), exact without windows; plan_ws covers the
+ * summaries (only when a head is dynamic) and the bitmaps (only when a head
+ * has a window). */
+vsa_status vsa_query_mixed(const vsa_shape* shape, const vsa_head_option* options, int estimator,
+                           int64_t* row_ptr_len, int64_t* col_capacity, size_t* plan_ws);
+
+/* Mixed per-head plan: row r = (b*heads + h)*NB + i of the CSR index is
+ * built by head h's option (Top-K with ties to the lower id, united with
+ * that head's window).  q, k: device [B, heads, N, D]; they may be NULL
+ * when no head is dynamic, and the index then depends on the table alone,
+ * so it can be built once and reused across calls.  static_scores: device
+ * float32 [heads][NB][NB] (row i, column j = the ranking score of key
+ * block j for query block i of head h, shared by every batch item), read
+ * only for static heads and otherwise may be NULL.  index->window_t is set
+ * to the largest head window.  Other arguments as in vsa_plan_select. */
+vsa_status vsa_plan_mixed(const void* q, const void* k, const vsa_shape* shape,
+                          const vsa_head_option* options, int estimator, const float* static_scores,
+                          vsa_index* index, void* ws, size_t ws_bytes, void* stream);
 
 /* Inter-block importance matrix of an estimator alone (SPADE 3.1 Fig. 4,
  * 3.3): q, k: device [B, heads, N, D]; out: device float32

@@ -296,3 +296,102 @@ def test_estimator_workspace_and_errors(lib):
     assert lib.vsa_estimate(FAKE, FAKE, ctypes.byref(shape), 3, FAKE, FAKE, 1 << 30, None) == _lib.VSA_ERR_INVALID_ARG
     assert lib.vsa_estimate(None, FAKE, ctypes.byref(shape), 1, FAKE, FAKE, 1 << 30, None) == _lib.VSA_ERR_INVALID_ARG
     assert lib.vsa_estimate(FAKE, FAKE, ctypes.byref(shape), 1, FAKE, FAKE, sizes[1] // 2, None) == _lib.VSA_ERR_WORKSPACE
+
+
+def _opts(*triples):
+    arr = (_lib.VsaHeadOption * len(triples))()
+    for h, (kind, value, win) in enumerate(triples):
+        arr[h] = _lib.VsaHeadOption(kind, value, win)
+    return arr
+
+
+def test_query_mixed_capacity_matches_oracle():
+    from oracle import mixed_oracle as M
+    lib = _lib.load()
+    w = W.custom("mx", 2, 3, 64, (9, 14, 20), (4, 4, 8), "f32", 0.5, -1, "iid")
+    shape = _shape(w)
+    g = O.geometry(w.grid, w.block)
+    triples = [(_lib.VSA_HEAD_DYNAMIC, 0.2, -1), (_lib.VSA_HEAD_STATIC, 0.3, -1), (_lib.VSA_HEAD_DENSE, 0.0, -1)]
+    rl, cap, pws = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
+    assert lib.vsa_query_mixed(ctypes.byref(shape), _opts(*triples), 0, ctypes.byref(rl), ctypes.byref(cap),
+                               ctypes.byref(pws)) == 0
+    inp = W.generate(w, seed=1)
+    table = np.random.default_rng(2).standard_normal((3, g.NB, g.NB)).astype(np.float32)
+    names = {0: "dynamic", 1: "static", 2: "dense"}
+    opts = [{"kind": names[t[0]], "value": t[1], "window_t": t[2]} for t in triples]
+    rp, ci, _ = M.plan_mixed(inp["q"], inp["k"], w.grid, w.block, opts, table)
+    assert rl.value == len(rp) and cap.value == len(ci)       # exact without windows
+    # static and dense heads only: no summaries, no workspace
+    assert lib.vsa_query_mixed(ctypes.byref(shape), _opts((1, 0.3, -1), (2, 0.0, -1), (1, 0.1, -1)), 0,
+                               None, None, ctypes.byref(pws)) == 0
+    assert pws.value == 0
+    # a window adds the bitmap regions
+    assert lib.vsa_query_mixed(ctypes.byref(shape), _opts((1, 0.3, 1), (2, 0.0, -1), (1, 0.1, -1)), 0,
+                               None, ctypes.byref(cap), ctypes.byref(pws)) == 0
+    assert pws.value > 0
+
+
+def test_mixed_entry_error_paths():
+    lib = _lib.load()
+    w = W.WORKLOADS["wan13b"]
+    shape = _shape(w)
+    ok = [(0, 0.2, -1)] * 12
+    q = lambda opts, est=0: lib.vsa_query_mixed(ctypes.byref(shape), _opts(*opts), est, None, None, None)
+    assert q(ok) == 0
+    assert q(ok, est=3) == _lib.VSA_ERR_INVALID_ARG
+    assert q([(3, 0.2, -1)] + ok[1:]) == _lib.VSA_ERR_INVALID_ARG
+    assert q([(0, 0.0, -1)] + ok[1:]) == _lib.VSA_ERR_INVALID_ARG
+    assert q([(1, 1.5, -1)] + ok[1:]) == _lib.VSA_ERR_INVALID_ARG
+    assert q([(2, 0.0, -2)] + ok[1:]) == _lib.VSA_ERR_INVALID_ARG
+    assert q([(2, 0.0, 40000)] + ok[1:]) == _lib.VSA_ERR_INVALID_ARG
+    assert q([(2, 0.0, 3)] + ok[1:]) == 0                      # dense ignores value
+    assert lib.vsa_query_mixed(ctypes.byref(shape), None, 0, None, None, None) == _lib.VSA_ERR_INVALID_ARG
+    rl, cap, pws = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
+    static = [(1, 0.2, -1)] * 12
+    assert lib.vsa_query_mixed(ctypes.byref(shape), _opts(*static), 0, ctypes.byref(rl), ctypes.byref(cap),
+                               ctypes.byref(pws)) == 0
+
+    def plan(opts, qk=FAKE, table=FAKE, cap_=cap.value, ws=FAKE, wsb=1 << 30):
+        idx = VsaIndex(shape, 0, 0, FAKE, FAKE, cap_)
+        return lib.vsa_plan_mixed(qk, qk, ctypes.byref(shape), _opts(*opts), 0, table, ctypes.byref(idx), ws, wsb,
+                                  None)
+
+    assert plan(static, table=None) == _lib.VSA_ERR_INVALID_ARG      # static head without a table
+    assert plan(ok, qk=None) == _lib.VSA_ERR_INVALID_ARG            # dynamic head without Q/K
+    assert plan(static, cap_=cap.value - 1) == _lib.VSA_ERR_CAPACITY
+    assert plan(ok, wsb=16) == _lib.VSA_ERR_WORKSPACE
+
+
+def _balanced_xcd_rows(NB, BH):
+    """The attention kernel's head-balanced order, restated per XCD: XCD x
+    takes from every head h a contiguous slice of a or a + 1 rows (NB =
+    8a + bx, the extra rows of head h going to XCDs (h*bx + t) mod 8), head
+    after head; its k-th workgroup (bid = 8k + x) runs the k-th row."""
+    a, bx = NB // 8, NB % 8
+    per_xcd = [[] for _ in range(8)]
+    for h in range(BH):
+        extra = [((x - h * bx) % 8) < bx for x in range(8)]
+        for x in range(8):
+            start = a * x + sum(extra[:x])
+            per_xcd[x] += [(h, start + j) for j in range(a + extra[x])]
+    return per_xcd
+
+
+@pytest.mark.parametrize("NB", [1, 4, 7, 8, 9, 36, 336, 1176])
+@pytest.mark.parametrize("BH", [1, 3, 12, 40])
+def test_balanced_xcd_mapping_is_a_bijection(NB, BH):
+    """Every (head, query block) row is run exactly once, each XCD gets
+    exactly the workgroups the hardware deals it (bid = x mod 8), and its
+    rows are contiguous slices of each head."""
+    nwg = NB * BH
+    per_xcd = _balanced_xcd_rows(NB, BH)
+    for x in range(8):
+        assert len(per_xcd[x]) == len(range(x, nwg, 8))
+    assert sorted(r for rows in per_xcd for r in rows) == [(h, i) for h in range(BH) for i in range(NB)]
+    for x in range(8):
+        heads = [h for h, _ in per_xcd[x]]
+        assert heads == sorted(heads)                       # head after head
+        for h in set(heads):
+            rows = [i for hh, i in per_xcd[x] if hh == h]
+            assert rows == list(range(rows[0], rows[0] + len(rows)))   # contiguous slice
+            assert len(rows) in (NB // 8, NB // 8 + 1)
