@@ -263,12 +263,22 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const Rsrc4 vrs = make_rsrc4(v + head_off, head_bytes);
   const uint32_t lds0 = (uint32_t)uniform((int)lds_addr(lds));
 
-  // This wave's queries: tokens [32*wave, +32) of the block (none past ni).
-  const bool active = uniform(32 * wave < ni) != 0;
+  // This wave's queries: tokens [32*qt, +32) of the block.  A block of at
+  // most 64 query tokens would leave waves idle, so there the waves split
+  // the key tiles instead: wave w takes query tile qt and key role kr --
+  // kr 0 runs tile 0 of every stage (the pipelined step below), kr 1 tile 1
+  // (one unpipelined step per stage) -- and the two partial softmax states
+  // of a query tile are merged through LDS after the last stage.  With one
+  // query tile, waves 2 and 3 stay idle.
+  const int split = uniform(ni <= 64 ? 1 : 0);
+  const int qtiles = (ni + 31) >> 5;
+  const int qt = uniform(split ? (qtiles == 2 ? (wave & 1) : 0) : wave);
+  const int kr = uniform(split ? (qtiles == 2 ? (wave >> 1) : (wave & 1)) : 0);
+  const bool active = uniform(split ? (qtiles == 2 || wave < 2) : (32 * wave < ni)) != 0;
   // Q^T fragments (B operand): query column l32, channels 16*ks + 8*g2 + [0, 8).
   bf16x8_t qf[D / 16];
   {
-    const int qtok = 32 * wave + l32;
+    const int qtok = 32 * qt + l32;
     const bool ok = qtok < ni;
     const uint16_t* qp = q + head_off + (size_t)(ok ? qmap(qtok) : 0) * D + g2 * 8;
 #pragma unroll
@@ -454,7 +464,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
   f32x16_t sc, st;   // scores of the tile to exponentiate next / the tile after it
-  if (active && nv0c > 0) {
+  if (active && kr == 0 && nv0c > 0) {
     sc = qk_tile<D>(lds + A0, kaddr, qf);
     if (nv0c < 32) mask_tile(sc, 0, nv0c, g2x4);
     m_run = half_max(tile_max(sc));   // O and l are still zero: no rescale
@@ -495,6 +505,31 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }                                                                                         \
   }
 
+  // One unpipelined step over the 32-key tile of K rows at KT and V rows at
+  // VT with NV valid keys (the key-split role kr 1): scores, mask, max with
+  // the lazy rescale, then probabilities into O and l.  m_run starts at
+  // -inf, so the first tile always takes the rescale, with alpha = 0.
+#define VSA_SOLO(S, KT, VT, NV)                                                               \
+  {                                                                                           \
+    S = qk_tile<D>((KT), kaddr, qf);                                                          \
+    if ((NV) < 32) mask_tile(S, 0, (NV), g2x4);                                               \
+    const float mx = half_max(tile_max(S));                                                   \
+    if (__ballot(mx > m_run + tau) != 0ull) {                                                 \
+      const float m_new = fmaxf(m_run, mx);                                                   \
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);               \
+      _Pragma("unroll") for (int c = 0; c < D / 32; ++c) acc[c] *= alpha;                      \
+      l_run *= alpha;                                                                         \
+      m_run = m_new;                                                                          \
+    }                                                                                         \
+    const float mb = m_run * scale_log2;                                                      \
+    __builtin_amdgcn_s_setprio(1);                                                            \
+    const bf16x8_t p0 = probs(S, 0, scale_log2, mb, l_run);                                   \
+    const bf16x8_t p1 = probs(S, 1, scale_log2, mb, l_run);                                   \
+    pv_step<D>((VT), vaddr, 0, p0, acc);                                                      \
+    pv_step<D>((VT), vaddr, 1, p1, acc);                                                      \
+    __builtin_amdgcn_s_setprio(0);                                                            \
+  }
+
   // Iteration t (P = t % 2).  Resident: K(t) tile 1 in B slot P, K(t+1)
   // tile 0 in A slot 1-P, V(t) in V slot P, all issued an iteration earlier;
   // sc holds the scores of stage t tile 0.  After the barrier every wave is
@@ -502,7 +537,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // 1-P (K(t-1) tile 1) and V slot 1-P (V(t-1)): V(t+1), K(t+1) tile 1 and
   // K(t+2) tile 0 go there.  A missing tile 1 (the row's last stage) reads
   // stale LDS, fully masked.
-#define VSA_ITER(P, OFF_NEXT, OFF_NEW)                                                        \
+#define VSA_ITER(P, OFF_NEXT, OFF_NEW, COMPUTE)                                               \
   {                                                                                           \
     __builtin_amdgcn_s_waitcnt(0x0F70);                                                       \
     __syncthreads();                                                                          \
@@ -518,19 +553,42 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const uint8_t* ka_ = lds + A0 + (1 - (P)) * HALF;   /* K(t+1) tile 0 */                 \
       const uint8_t* kb_ = lds + B0 + (P) * HALF;         /* K(t) tile 1 */                   \
       const uint8_t* v0_ = lds + V0 + (P) * TILE;         /* V(t) rows 0..31 */               \
-      VSA_STEP(sc, st, v0_, kb_, true, nv1c)                                                  \
-      VSA_STEP(st, sc, v0_ + 32 * ROW, ka_, nv0n > 0, nv0n)                                   \
+      COMPUTE                                                                                 \
     }                                                                                         \
     nv0c = nv0n; nv1c = nv1n;                                                                 \
     nv0n = nv0nn; nv1n = nv1nn;                                                               \
   }
 
-  while (nv0c > 0) {
-    VSA_ITER(0, offB, offA);
-    if (nv0c == 0) break;
-    VSA_ITER(1, offA, offB);
+  // Both tiles of every stage (a full query block), or one tile per stage
+  // and role (the key split); two loops, so that neither path's registers
+  // constrain the other's.
+#define VSA_BOTH                                                                              \
+  VSA_STEP(sc, st, v0_, kb_, true, nv1c)                                                      \
+  VSA_STEP(st, sc, v0_ + 32 * ROW, ka_, nv0n > 0, nv0n)
+#define VSA_ROLE                                                                              \
+  if (kr == 0) {                                                                              \
+    VSA_STEP(sc, st, v0_, ka_, nv0n > 0, nv0n)                                                \
+    sc = st;                                                                                  \
+  } else if (nv1c > 0) {                                                                      \
+    VSA_SOLO(st, kb_, v0_ + 32 * ROW, nv1c)                                                   \
   }
+  if (!split) {
+    while (nv0c > 0) {
+      VSA_ITER(0, offB, offA, VSA_BOTH);
+      if (nv0c == 0) break;
+      VSA_ITER(1, offA, offB, VSA_BOTH);
+    }
+  } else {
+    while (nv0c > 0) {
+      VSA_ITER(0, offB, offA, VSA_ROLE);
+      if (nv0c == 0) break;
+      VSA_ITER(1, offA, offB, VSA_ROLE);
+    }
+  }
+#undef VSA_BOTH
+#undef VSA_ROLE
 #undef VSA_ITER
+#undef VSA_SOLO
 #undef VSA_STEP
 #undef VSA_ISSUE_V
 #undef VSA_ISSUE_K1
@@ -539,11 +597,44 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #undef VSA_OPEN_BLOCK
 #undef VSA_ADVANCE
 
+  // Key split: the kr 1 wave of each query tile leaves O, m and l in LDS
+  // (the rings are free once every wave is past the last stage); the kr 0
+  // wave rescales both states to the larger max and adds them.  The kr 0
+  // wave always has a tile (the row's first); the kr 1 wave may have none
+  // (m = -inf, weight 0).
+  if (split) {
+    constexpr int NREG = (D / 32) * 16;   // accumulator floats per lane
+    static_assert(2 * (NREG + 2) * 64 * 4 <= 4 * TILE, "two exchange regions must fit in the rings");
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    float* xch = reinterpret_cast<float*>(lds) + qt * (NREG + 2) * 64 + lane;
+    if (active && kr == 1) {
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xch[(c * 16 + r) * 64] = acc[c][r];
+      xch[NREG * 64] = m_run;
+      xch[(NREG + 1) * 64] = l_run;
+    }
+    __syncthreads();
+    if (active && kr == 0) {
+      const float m1 = xch[NREG * 64], l1 = xch[(NREG + 1) * 64];
+      const float m = fmaxf(m_run, m1);
+      const float a0 = __builtin_amdgcn_exp2f((m_run - m) * scale_log2);
+      const float a1 = __builtin_amdgcn_exp2f((m1 - m) * scale_log2);
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[c][r] = acc[c][r] * a0 + xch[(c * 16 + r) * 64] * a1;
+      l_run = l_run * a0 + l1 * a1;
+    }
+  }
+
   // Epilogue: O = O^T / l, rounded to bf16, stored at the query's raster row.
-  {
+  if (kr == 0) {
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    const int qtok = 32 * wave + l32;
-    if (qtok < ni) {
+    const int qtok = 32 * qt + l32;
+    if (active && qtok < ni) {
       const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
       uint16_t* op = o + head_off + (size_t)qmap(qtok) * D;
 #pragma unroll
