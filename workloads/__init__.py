@@ -29,7 +29,9 @@ the tensors stand in for post-RoPE Q/K/V of one attention layer):
 Recipe (seed 0 everywhere):
 
 * ``tiny_fp32``: ``rng = default_rng(0)``; q, k, v drawn in that order as
-  ``standard_normal((1, 2, 256, 64))`` cast to float32.
+  ``standard_normal((1, 2, 256, 64))`` cast to float32.  Other ``iid``
+  workloads draw the same way at their own shape and, when their dtype is
+  bf16, are rounded to bfloat16 (RNE) like the smooth ones.
 * others: ``SeedSequence(0).spawn(4)`` gives independent PCG64 streams for
   (Q, K, V, densities).  Q and K are smooth fields plus noise,
   X[b,h,t,y,x,c] = 0.5*eps + sum_{m<4} cos(2*pi*(ft*t + fh*y + fw*x) + phi),
@@ -147,6 +149,8 @@ def generate(w: Workload, seed: int = 0) -> Dict[str, object]:
         k = rng.standard_normal(shape).astype(np.float32)
         v = rng.standard_normal(shape).astype(np.float32)
         dens = np.full(w.heads, w.density, dtype=np.float32)
+        if w.dtype == "bf16":
+            q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
     else:
         sq, sk, sv, sd = np.random.SeedSequence(seed).spawn(4)
         q = _smooth_field(np.random.default_rng(sq), w.B, w.heads, w.D, w.grid)
