@@ -246,6 +246,58 @@ __device__ inline void est_column(const float* __restrict__ qa, const float* __r
   }
 }
 
+// The box estimators' scores with the RT query summaries staged in LDS
+// (qa_s, qb_s: [RT][D] floats) and the key box read 32 channels at a time,
+// so a column waits for D/32 pairs of loads instead of D/4.  The per-score
+// order is unchanged: channels ascending, each term added on its own.  (The
+// mean estimator keeps est_column: its query means come through scalar
+// loads, which staging in LDS only slows down.)
+template <int EST, int RT>
+__device__ inline void est_column_staged(const float* qa_s, const float* qb_s, const float* __restrict__ ka,
+                                         const float* __restrict__ kb, int D, float (&acc)[RT]) {
+#pragma unroll
+  for (int r = 0; r < RT; ++r) acc[r] = 0.0f;
+  for (int d0 = 0; d0 < D; d0 += 32) {
+    float4 kA[8], kB[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      kA[u] = *reinterpret_cast<const float4*>(ka + d0 + 4 * u);
+      if constexpr (EST != 0) kB[u] = *reinterpret_cast<const float4*>(kb + d0 + 4 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const float4 qA = *reinterpret_cast<const float4*>(qa_s + r * D + d0 + 4 * u);
+        if constexpr (EST == 0) {
+          acc[r] = __fadd_rn(acc[r], __fmul_rn(qA.x, kA[u].x));
+          acc[r] = __fadd_rn(acc[r], __fmul_rn(qA.y, kA[u].y));
+          acc[r] = __fadd_rn(acc[r], __fmul_rn(qA.z, kA[u].z));
+          acc[r] = __fadd_rn(acc[r], __fmul_rn(qA.w, kA[u].w));
+        } else if constexpr (EST == 1) {
+          acc[r] = __fadd_rn(acc[r], fmaxf(__fmul_rn(qA.x, kA[u].x), __fmul_rn(qA.x, kB[u].x)));
+          acc[r] = __fadd_rn(acc[r], fmaxf(__fmul_rn(qA.y, kA[u].y), __fmul_rn(qA.y, kB[u].y)));
+          acc[r] = __fadd_rn(acc[r], fmaxf(__fmul_rn(qA.z, kA[u].z), __fmul_rn(qA.z, kB[u].z)));
+          acc[r] = __fadd_rn(acc[r], fmaxf(__fmul_rn(qA.w, kA[u].w), __fmul_rn(qA.w, kB[u].w)));
+        } else {
+          const float4 qB = *reinterpret_cast<const float4*>(qb_s + r * D + d0 + 4 * u);
+          acc[r] = __fadd_rn(acc[r], fmaxf(fmaxf(__fmul_rn(qA.x, kA[u].x), __fmul_rn(qA.x, kB[u].x)),
+                                           fmaxf(__fmul_rn(qB.x, kA[u].x), __fmul_rn(qB.x, kB[u].x))));
+          acc[r] = __fadd_rn(acc[r], fmaxf(fmaxf(__fmul_rn(qA.y, kA[u].y), __fmul_rn(qA.y, kB[u].y)),
+                                           fmaxf(__fmul_rn(qB.y, kA[u].y), __fmul_rn(qB.y, kB[u].y))));
+          acc[r] = __fadd_rn(acc[r], fmaxf(fmaxf(__fmul_rn(qA.z, kA[u].z), __fmul_rn(qA.z, kB[u].z)),
+                                           fmaxf(__fmul_rn(qB.z, kA[u].z), __fmul_rn(qB.z, kB[u].z))));
+          acc[r] = __fadd_rn(acc[r], fmaxf(fmaxf(__fmul_rn(qA.w, kA[u].w), __fmul_rn(qA.w, kB[u].w)),
+                                           fmaxf(__fmul_rn(qB.w, kA[u].w), __fmul_rn(qB.w, kB[u].w))));
+        }
+      }
+    }
+  }
+}
+
+// Floats of LDS before the staged query summaries (16-byte aligned).
+__host__ __device__ inline int staged_q_offset(int RT, int NB) { return (RT * NB + 3) & ~3; }
+
 // Orderable key of a score: larger float -> larger key; -0 and +0 map to
 // the same key, so they tie (and the lower block id wins).
 __device__ inline uint32_t order_key(float s) {
@@ -449,7 +501,7 @@ __global__ __launch_bounds__(256) void score_select_kernel(
     Summaries sm, DGeo g, int D, int heads,
     SelectArgs sa, int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
     int32_t* __restrict__ counts, uint64_t* __restrict__ bits) {
-  extern __shared__ uint32_t smem[];   // [RT][NB] keys
+  extern __shared__ uint32_t smem[];   // [RT][NB] keys, then (RT >= 2) the staged query summaries
   const int NB = g.NB;
   const int bh = blockIdx.y;
   const int i0 = blockIdx.x * RT;
@@ -473,6 +525,20 @@ __global__ __launch_bounds__(256) void score_select_kernel(
   } else if (kind == 2) {
     for (int r = 0; r < rows_here; ++r)
       for (int j = tid; j < NB; j += 256) smem[r * NB + j] = 0x80000000u;
+  } else if (EST != 0 && RT >= 2 && rows_here == RT) {
+    float* qa_s = reinterpret_cast<float*>(smem) + staged_q_offset(RT, NB);
+    float* qb_s = qa_s + RT * D;
+    for (int x = tid; x < RT * D; x += 256) {
+      qa_s[x] = qa[(size_t)i0 * D + x];
+      if constexpr (EST == 2) qb_s[x] = qb[(size_t)i0 * D + x];
+    }
+    __syncthreads();
+    for (int j = tid; j < NB; j += 256) {
+      float acc[RT];
+      est_column_staged<EST, RT>(qa_s, qb_s, ka + (size_t)j * D, kb + (EST != 0 ? (size_t)j * D : 0), D, acc);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) smem[r * NB + j] = order_key(acc[r]);
+    }
   } else if (rows_here == RT) {
     for (int j = tid; j < NB; j += 256) {
       float acc[RT];
@@ -634,11 +700,18 @@ hipError_t launch_pool(const void* x0, float* out0, const void* x1, float* out1,
   return hipGetLastError();
 }
 
-int select_rows_per_block(int NB) {
-  // RT rows of NB uint32 keys must fit in 64 KiB of LDS (plus 4 KiB of query means).
-  if (NB * 8 * 4 <= 65536) return 8;
-  if (NB * 4 * 4 <= 65536) return 4;
-  if (NB * 2 * 4 <= 65536) return 2;
+// LDS of a workgroup with RT rows: RT rows of NB uint32 keys, and for the
+// box estimators with RT >= 2 the staged query summaries (RT x D floats, two
+// sets for DSA2).
+size_t select_lds_bytes(int RT, int NB, int D, int est) {
+  if (est == 0 || RT < 2) return (size_t)RT * NB * 4;
+  return (size_t)staged_q_offset(RT, NB) * 4 + (size_t)RT * D * 4 * (est == 2 ? 2 : 1);
+}
+
+// Rows per workgroup: the most rows whose LDS fits in 64 KiB.
+int select_rows_per_block(int NB, int D, int est) {
+  for (int RT = 8; RT >= 2; RT >>= 1)
+    if (select_lds_bytes(RT, NB, D, est) <= 65536) return RT;
   return 1;
 }
 
@@ -667,9 +740,9 @@ void launch_score_select_e(int RT, dim3 grid, dim3 block, size_t lds, hipStream_
 hipError_t launch_score_select(const Summaries& sm, int est, const DGeo& g, int D, int heads, int BH,
                                const SelectArgs& sa, int32_t* row_ptr, int32_t* col_idx, int32_t* counts,
                                uint64_t* bits, hipStream_t st) {
-  const int RT = select_rows_per_block(g.NB);
+  const int RT = select_rows_per_block(g.NB, D, est);
   dim3 grid((g.NB + RT - 1) / RT, BH), block(256);
-  size_t lds = (size_t)RT * g.NB * sizeof(uint32_t);
+  const size_t lds = select_lds_bytes(RT, g.NB, D, est);
   if (est == 1)
     launch_score_select_e<1>(RT, grid, block, lds, st, sm, g, D, heads, sa, row_ptr, col_idx, counts, bits);
   else if (est == 2)
