@@ -111,7 +111,8 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ x0, flo
 
 // ---------------------------------------------------------------------------
 // Block extremes (the max/min summarizer).  Same walk as pool_kernel; a
-// load past the block's last token is skipped rather than added.  For a
+// slot past the block's last token re-reads the block's first token, which
+// leaves max and min unchanged, so the reduction needs no predicate.  For a
 // tensor with `mid` set the query midpoint fl(fl(max + min) * 0.5) goes to
 // omax and omin is not written.  max and min are exact.
 // ---------------------------------------------------------------------------
@@ -135,7 +136,8 @@ __global__ __launch_bounds__(256) void extremes_kernel(const T* __restrict__ x0,
   const int n = uniform_i(b.n());
   const __amdgpu_buffer_rsrc_t rs = plan_rsrc(x + (size_t)bh * g.N * D, (uint32_t)g.N * ROWB);
   const int voff = lane * C * (int)sizeof(T);
-  int soff = uniform_i(((b.t0 * g.H + b.h0) * g.W + b.w0) * ROWB);
+  const int soff0 = uniform_i(((b.t0 * g.H + b.h0) * g.W + b.w0) * ROWB);
+  int soff = soff0;
   int uh = 0, uw = 0;
   const int ew = uniform_i(b.ew), eh = uniform_i(b.eh);
   const int wrap_w = uniform_i((g.W - b.ew) * ROWB), wrap_h = uniform_i((g.H - b.eh) * g.W * ROWB);
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(256) void extremes_kernel(const T* __restrict__ x0,
     float v[PF][C];
 #pragma unroll
     for (int e = 0; e < PF; ++e) {
-      load_token<T, C>(rs, voff, u0 + e < n ? soff : (int)0x80000000, v[e]);
+      load_token<T, C>(rs, voff, u0 + e < n ? soff : soff0, v[e]);
       soff += ROWB;
       if (++uw == ew) {
         uw = 0;
@@ -162,11 +164,10 @@ __global__ __launch_bounds__(256) void extremes_kernel(const T* __restrict__ x0,
     }
 #pragma unroll
     for (int e = 0; e < PF; ++e) {
-      const bool ok = u0 + e < n;
 #pragma unroll
       for (int c = 0; c < C; ++c) {
-        mx[c] = ok ? fmaxf(mx[c], v[e][c]) : mx[c];
-        mn[c] = ok ? fminf(mn[c], v[e][c]) : mn[c];
+        mx[c] = fmaxf(mx[c], v[e][c]);
+        mn[c] = fminf(mn[c], v[e][c]);
       }
     }
   }

@@ -107,18 +107,19 @@ __global__ __launch_bounds__(256) void sics_kernel(const T* __restrict__ x0, flo
 }
 
 // ---------------------------------------------------------------------------
-// Aggregation scores and selection.  One wave per row bh: for each
-// candidate, AS(Q) and AS(K) are sums over that candidate's block SICS in a
+// Aggregation scores and selection.  One workgroup per row bh, one wave per
+// candidate: AS(Q) and AS(K) are sums over that candidate's block SICS in a
 // fixed order (lane-strided partial sums, then a butterfly), so the result
-// and the choice are reproducible; the first candidate with the highest
-// AS(Q) + AS(K) wins.
+// and the choice are reproducible; after a barrier one thread takes the
+// first candidate with the highest AS(Q) + AS(K).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void scheme_select_kernel(const float* __restrict__ sics, SchemeArgs sa, int BH,
-                                                           float* __restrict__ scores, int32_t* __restrict__ choice) {
-  const int bh = blockIdx.x, lane = threadIdx.x;
-  float best = -INFINITY;
-  int best_c = 0;
-  for (int c = 0; c < sa.n; ++c) {
+__global__ __launch_bounds__(64 * VSA_MAX_SCHEMES) void scheme_select_kernel(const float* __restrict__ sics,
+                                                                             SchemeArgs sa, int BH,
+                                                                             float* __restrict__ scores,
+                                                                             int32_t* __restrict__ choice) {
+  __shared__ float sc_s[VSA_MAX_SCHEMES];
+  const int bh = blockIdx.x, lane = threadIdx.x & 63, c = threadIdx.x >> 6;
+  if (c < sa.n) {
     const int nb = sa.nb[c];
     float tot[2];
 #pragma unroll
@@ -131,13 +132,23 @@ __global__ __launch_bounds__(64) void scheme_select_kernel(const float* __restri
       tot[t] = a;
     }
     const float sc = tot[0] + tot[1];
-    if (lane == 0) scores[(size_t)c * BH + bh] = sc;
-    if (sc > best) {
-      best = sc;
-      best_c = c;
+    if (lane == 0) {
+      scores[(size_t)c * BH + bh] = sc;
+      sc_s[c] = sc;
     }
   }
-  if (lane == 0) choice[bh] = best_c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float best = -INFINITY;
+    int best_c = 0;
+    for (int k = 0; k < sa.n; ++k) {
+      if (sc_s[k] > best) {
+        best = sc_s[k];
+        best_c = k;
+      }
+    }
+    choice[bh] = best_c;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -167,7 +178,7 @@ hipError_t launch_sics(const void* x0, float* out0, const void* x1, float* out1,
 
 hipError_t launch_scheme_select(const float* sics, const SchemeArgs& sa, int BH, float* scores, int32_t* choice,
                                 hipStream_t st) {
-  hipLaunchKernelGGL(scheme_select_kernel, dim3(BH), dim3(64), 0, st, sics, sa, BH, scores, choice);
+  hipLaunchKernelGGL(scheme_select_kernel, dim3(BH), dim3(64 * sa.n), 0, st, sics, sa, BH, scores, choice);
   return hipGetLastError();
 }
 
