@@ -308,13 +308,16 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // stage is two consecutive tiles of the row's tile sequence, so a stage
   // may take its tiles from two blocks (of at most 32 tokens each).  The
   // block ids of the next two entries are fetched ahead into jn1/jn2 by
-  // vector loads; a block is opened at least one iteration after its id
-  // was requested, so the iteration's wait has already covered the load.
+  // scalar loads (the ids are wave-uniform).  A scalar load is waited on
+  // through lgkmcnt, which the K/V loads to LDS do not touch: a vector load
+  // here would make the compiler's wait for the id (vmcnt, which does not
+  // see the inline-asm K/V loads) also wait for the stage just issued.
+  // Entries are read only below e_end, inside the row.
   const int row = bh * g.NB + i;
   const int e_end = uniform(row_ptr[row + 1]);
   int e_ld = uniform(row_ptr[row]);
-  const __amdgpu_buffer_rsrc_t cirs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)col_idx, (short)0, e_end * 4, 0x00020000);
+  const __attribute__((address_space(4))) int32_t* cid_s =
+      (const __attribute__((address_space(4))) int32_t*)(uintptr_t)col_idx;
   int c_ld = 0, nj = 0;
   uint32_t jbase = 0, ltype = 0;
   int jn1 = 0, jn2 = 0;
@@ -340,7 +343,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
       if (e_ld < e_end) {                                                                     \
         VSA_OPEN_BLOCK(__builtin_amdgcn_readfirstlane(jn1));                                  \
         jn1 = jn2;                                                                            \
-        if (e_ld + 2 < e_end) jn2 = __builtin_amdgcn_raw_buffer_load_b32(cirs, (e_ld + 2) * 4, 0, 0); \
+        if (e_ld + 2 < e_end) jn2 = cid_s[e_ld + 2];                                           \
       }                                                                                       \
     }                                                                                         \
   } while (0)
@@ -445,9 +448,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   __syncthreads();   // tok_tbl complete
   if (e_ld < e_end) {
-    VSA_OPEN_BLOCK(col_idx[e_ld]);
-    if (e_ld + 1 < e_end) jn1 = __builtin_amdgcn_raw_buffer_load_b32(cirs, (e_ld + 1) * 4, 0, 0);
-    if (e_ld + 2 < e_end) jn2 = __builtin_amdgcn_raw_buffer_load_b32(cirs, (e_ld + 2) * 4, 0, 0);
+    VSA_OPEN_BLOCK(cid_s[e_ld]);
+    if (e_ld + 1 < e_end) jn1 = cid_s[e_ld + 1];
+    if (e_ld + 2 < e_end) jn2 = cid_s[e_ld + 2];
   }
 
   // Prologue: all of stage 0 and K tile 0 of stage 1; S^T of stage 0 tile 0.
