@@ -15,6 +15,11 @@
  *      united with a local temporal window (3.3);
  *   4. attention (Eq. 2) runs over the kept blocks only with an online
  *      softmax, and the output is restored to raster order (3.3).
+ * Around that path (3.1-3.3): Top-P selection and attention-sink blocks,
+ * the max/min (DSA, DSA2) summarizers and estimators, mixed per-head plans
+ * (dense, static and dynamic heads with their own windows), and scheme
+ * generation (per-block intra-block aggregation and head-wise selection of
+ * a blocking scheme, 3.2).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
