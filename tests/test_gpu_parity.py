@@ -81,6 +81,9 @@ SMALL = [
     W.custom("s_single_block", 1, 2, 128, (2, 3, 5), (4, 4, 8), "bf16", 1.0, -1, "smooth"),
     W.custom("s_token_blocks", 1, 1, 128, (4, 4, 4), (1, 1, 1), "bf16", 0.25, -1, "smooth"),
     W.custom("s_dense_bf16", 1, 2, 128, (4, 8, 16), (2, 4, 8), "bf16", 1.0, -1, "smooth"),
+    # batch 2 with query blocks of 128, 64, 32 and 16 tokens (the key split covers the short ones)
+    W.custom("s_batch2_short_bf16", 2, 2, 128, (9, 10, 12), (4, 4, 8), "bf16", 0.4, -1, "smooth"),
+    W.custom("s_batch2_short_d64", 2, 3, 64, (5, 6, 20), (2, 4, 8), "bf16", 0.5, 0, "smooth"),
 ]
 
 
