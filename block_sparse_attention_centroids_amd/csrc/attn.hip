@@ -602,9 +602,10 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   // Key split: the kr 1 wave of each query tile leaves O, m and l in LDS
   // (the rings are free once every wave is past the last stage); the kr 0
-  // wave rescales both states to the larger max and adds them.  The kr 0
-  // wave always has a tile (the row's first); the kr 1 wave may have none
-  // (m = -inf, weight 0).
+  // wave rescales both states to the larger max and adds them.  A wave that
+  // saw no key (the kr 1 wave of a single-tile row, or both waves of an
+  // empty row in an index built by hand) has m = -inf and gets weight 0; an
+  // empty row keeps O = 0 and l = 0, as in the unsplit path.
   if (split) {
     constexpr int NREG = (D / 32) * 16;   // accumulator floats per lane
     static_assert(2 * (NREG + 2) * 64 * 4 <= 4 * TILE, "two exchange regions must fit in the rings");
@@ -623,8 +624,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
     if (active && kr == 0) {
       const float m1 = xch[NREG * 64], l1 = xch[(NREG + 1) * 64];
       const float m = fmaxf(m_run, m1);
-      const float a0 = __builtin_amdgcn_exp2f((m_run - m) * scale_log2);
-      const float a1 = __builtin_amdgcn_exp2f((m1 - m) * scale_log2);
+      const float a0 = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m_run - m) * scale_log2);
+      const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m1 - m) * scale_log2);
 #pragma unroll
       for (int c = 0; c < D / 32; ++c)
 #pragma unroll
@@ -717,7 +718,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
   }
   if (active) {
     float* op = o + head_off + (size_t)qmap(tid) * D;
-    const float inv = 1.0f / l_run;
+    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;   // an empty row gives zeros
 #pragma unroll
     for (int d = 0; d < D; ++d) op[d] = ov[d] * inv;
   }

@@ -248,7 +248,9 @@ vsa_status vsa_estimate(const void* q, const void* k, const vsa_shape* shape, in
  * q, k, v, o: device [B, heads, N, D] in index->shape; o is written in
  * raster order.  scale: logit scale, 0 means 1/sqrt(D).  bf16 uses bf16
  * matrix cores with float32 accumulation and a float32 online softmax; f32
- * computes in float32.  ws may be NULL when attn_ws is 0. */
+ * computes in float32.  A row of the index with no key blocks (never
+ * produced by the planners) gives zeros for its query tokens.  ws may be
+ * NULL when attn_ws is 0. */
 vsa_status vsa_attn(const void* q, const void* k, const void* v, const vsa_index* index,
                     float scale, void* o, void* ws, size_t ws_bytes, void* stream);
 
