@@ -50,8 +50,8 @@ hipError_t summarize(const void* q, const void* k, const vsa_shape* shape, const
   float* s2 = ps.n_sum > 2 ? reinterpret_cast<float*>(w + ps.off_sum[2]) : nullptr;
   float* s3 = ps.n_sum > 3 ? reinterpret_cast<float*>(w + ps.off_sum[3]) : nullptr;
   if (ps.estimator == VSA_EST_MEAN) {
-    *sm = Summaries{s0, nullptr, s1, nullptr};
-    return launch_pool(q, s0, k, s1, shape->dtype, shape->D, dg, BH, st);
+    *sm = Summaries{s0, nullptr, s1, nullptr, 1};
+    return launch_pool(q, s0, k, s1, shape->dtype, shape->D, dg, BH, st, true);
   }
   if (ps.estimator == VSA_EST_DSA) {
     *sm = Summaries{s0, nullptr, s1, s2};

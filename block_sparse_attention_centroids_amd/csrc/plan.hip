@@ -60,7 +60,7 @@ __device__ inline void load_token(__amdgpu_buffer_rsrc_t rs, int voff, int soff,
 template <typename T, int D>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ x0, float* __restrict__ out0,
                                                    const T* __restrict__ x1, float* __restrict__ out1,
-                                                   DGeo g, int nitems) {
+                                                   DGeo g, int nitems, int cm1) {
   constexpr int C = D / 64;   // channels per lane
   constexpr int PF = 32;      // token loads in flight per wave
   constexpr int ROWB = D * (int)sizeof(T);
@@ -104,9 +104,15 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ x0, flo
 #pragma unroll
       for (int c = 0; c < C; ++c) acc[c] = __fadd_rn(acc[c], v[e][c]);
   }
-  float* o = out + (size_t)item * D + lane * C;
+  if (blockIdx.y && cm1) {   // channel-major: channel d of block j at [bh][d][j]
+    float* o = out + ((size_t)bh * D + lane * C) * g.NB + j;
 #pragma unroll
-  for (int c = 0; c < C; ++c) o[c] = __fdiv_rn(acc[c], (float)n);
+    for (int c = 0; c < C; ++c) o[(size_t)c * g.NB] = __fdiv_rn(acc[c], (float)n);
+  } else {
+    float* o = out + (size_t)item * D + lane * C;
+#pragma unroll
+    for (int c = 0; c < C; ++c) o[c] = __fdiv_rn(acc[c], (float)n);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -201,6 +207,30 @@ __device__ inline void score_column(const float* __restrict__ qrows, const float
       acc[r] = __fadd_rn(acc[r], __fmul_rn(qv.y, kv.y));
       acc[r] = __fadd_rn(acc[r], __fmul_rn(qv.z, kv.z));
       acc[r] = __fadd_rn(acc[r], __fmul_rn(qv.w, kv.w));
+    }
+  }
+}
+
+// Mean scores of RG query rows (qr[x]: D floats each, the same for the whole
+// wave, so they come through scalar loads) against the key block whose
+// channel d is at kj[d * sd]: the same products and the same channel order
+// as score_column, for either key-mean layout.
+template <int RG>
+__device__ inline void mean_column(const float* const (&qr)[RG], const float* __restrict__ kj, size_t sd,
+                                   int D, float (&acc)[RG]) {
+#pragma unroll
+  for (int x = 0; x < RG; ++x) acc[x] = 0.0f;
+#pragma unroll 4
+  for (int d = 0; d < D; d += 4) {
+    const float k0 = kj[(size_t)d * sd], k1 = kj[(size_t)(d + 1) * sd];
+    const float k2 = kj[(size_t)(d + 2) * sd], k3 = kj[(size_t)(d + 3) * sd];
+#pragma unroll
+    for (int x = 0; x < RG; ++x) {
+      const float4 qv = *reinterpret_cast<const float4*>(qr[x] + d);
+      acc[x] = __fadd_rn(acc[x], __fmul_rn(qv.x, k0));
+      acc[x] = __fadd_rn(acc[x], __fmul_rn(qv.y, k1));
+      acc[x] = __fadd_rn(acc[x], __fmul_rn(qv.z, k2));
+      acc[x] = __fadd_rn(acc[x], __fmul_rn(qv.w, k3));
     }
   }
 }
@@ -335,27 +365,40 @@ __device__ inline uint32_t wave_max_u(uint32_t v) {
 // Top-K cut of a row of keys: thr = the k-th largest key, need = how many
 // keys equal to thr are kept (the lowest ids).  thr grows bit by bit from
 // the top to the largest value with at least kk keys >= thr; counts are
-// ballots, and rows of at most 512 blocks keep their keys in registers.
+// ballots, and rows of at most 512 blocks keep their keys in registers
+// (4, 6 or 8 chunks of 64, the fewest that hold the row).
+template <int NR>
+__device__ inline uint32_t topk_threshold_regs(const uint32_t* keys, int NB, int lane, int kk, int& gt) {
+  uint32_t kv[NR];
+#pragma unroll
+  for (int s2 = 0; s2 < NR; ++s2) {
+    const int j = s2 * 64 + lane;
+    kv[s2] = j < NB ? keys[j] : 0u;   // below every real key
+  }
+  uint32_t thr = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int s2 = 0; s2 < NR; ++s2) cnt += __popcll(__ballot(kv[s2] >= cand));
+    if (cnt >= kk) thr = cand;
+  }
+  gt = 0;
+#pragma unroll
+  for (int s2 = 0; s2 < NR; ++s2) gt += __popcll(__ballot(kv[s2] > thr));
+  return thr;
+}
+
 __device__ inline void topk_cut(const uint32_t* keys, int NB, int lane, int kk, uint32_t& thr_out,
                                 int& need_out) {
   uint32_t thr = 0u;
   int gt = 0;
-  if (NB <= 64 * 8) {
-    uint32_t kv[8];
-#pragma unroll
-    for (int s2 = 0; s2 < 8; ++s2) {
-      const int j = s2 * 64 + lane;
-      kv[s2] = j < NB ? keys[j] : 0u;   // below every real key
-    }
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = thr | (1u << bit);
-      int cnt = 0;
-#pragma unroll
-      for (int s2 = 0; s2 < 8; ++s2) cnt += __popcll(__ballot(kv[s2] >= cand));
-      if (cnt >= kk) thr = cand;
-    }
-#pragma unroll
-    for (int s2 = 0; s2 < 8; ++s2) gt += __popcll(__ballot(kv[s2] > thr));
+  if (NB <= 64 * 4) {
+    thr = topk_threshold_regs<4>(keys, NB, lane, kk, gt);
+  } else if (NB <= 64 * 6) {
+    thr = topk_threshold_regs<6>(keys, NB, lane, kk, gt);
+  } else if (NB <= 64 * 8) {
+    thr = topk_threshold_regs<8>(keys, NB, lane, kk, gt);
   } else {
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = thr | (1u << bit);
@@ -526,7 +569,31 @@ __global__ __launch_bounds__(256) void score_select_kernel(
   } else if (kind == 2) {
     for (int r = 0; r < rows_here; ++r)
       for (int j = tid; j < NB; j += 256) smem[r * NB + j] = 0x80000000u;
-  } else if (EST != 0 && RT >= 2 && rows_here == RT) {
+  } else if (EST == 0) {
+    // Mean scores.  A task is RG rows x 64 consecutive key blocks (lane =
+    // key block) and the tasks are dealt evenly to the waves; with the
+    // channel-major key means every load of a channel is 256 contiguous
+    // bytes.  Rows past rows_here read the last row and are not stored.
+    constexpr int RG = RT < 4 ? RT : 4;
+    const int wv = uniform_i(wave);
+    const int chunks = (NB + 63) >> 6;
+    const int tasks = chunks * ((rows_here + RG - 1) / RG);
+    const size_t sj = sm.kt ? 1 : (size_t)D, sd = sm.kt ? (size_t)NB : 1;
+    for (int task = wv; task < tasks; task += 4) {
+      const int rg = task / chunks, ch = task - rg * chunks;
+      const int j = ch * 64 + lane;
+      const float* qr[RG];
+#pragma unroll
+      for (int x = 0; x < RG; ++x) qr[x] = qa + (size_t)(i0 + min(rg * RG + x, rows_here - 1)) * D;
+      float acc[RG];
+      mean_column<RG>(qr, ka + (size_t)min(j, NB - 1) * sj, sd, D, acc);
+      if (j < NB) {
+#pragma unroll
+        for (int x = 0; x < RG; ++x)
+          if (rg * RG + x < rows_here) smem[(rg * RG + x) * NB + j] = order_key(acc[x]);
+      }
+    }
+  } else if (RT >= 2 && rows_here == RT) {
     float* qa_s = reinterpret_cast<float*>(smem) + staged_q_offset(RT, NB);
     float* qb_s = qa_s + RT * D;
     for (int x = tid; x < RT * D; x += 256) {
@@ -670,8 +737,13 @@ __global__ __launch_bounds__(256) void scores_kernel(Summaries sm, float* __rest
   for (int j = threadIdx.x; j < NB; j += 256) {
     float acc[1];
     const size_t kj = head + (size_t)j * D;
-    est_column<EST, 1>(sm.qa + qi, EST == 2 ? sm.qb + qi : nullptr, sm.ka + kj, EST != 0 ? sm.kb + kj : nullptr,
-                       D, acc);
+    if constexpr (EST == 0) {
+      const float* qr[1] = {sm.qa + qi};
+      mean_column<1>(qr, sm.ka + (sm.kt ? head + j : kj), sm.kt ? (size_t)NB : 1, D, acc);
+    } else {
+      est_column<EST, 1>(sm.qa + qi, EST == 2 ? sm.qb + qi : nullptr, sm.ka + kj, EST != 0 ? sm.kb + kj : nullptr,
+                         D, acc);
+    }
     out[((size_t)bh * NB + i) * NB + j] = acc[0];
   }
 }
@@ -680,23 +752,24 @@ __global__ __launch_bounds__(256) void scores_kernel(Summaries sm, float* __rest
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_pool(const void* x0, float* out0, const void* x1, float* out1, int dtype, int D,
-                       const DGeo& g, int BH, hipStream_t st) {
+                       const DGeo& g, int BH, hipStream_t st, bool out1_channel_major) {
   const int nitems = BH * g.NB;
+  const int cm1 = out1_channel_major ? 1 : 0;
   dim3 grid((nitems + 3) / 4, x1 ? 2 : 1), block(256);
   if (dtype == 0) {
     if (D == 128)
       hipLaunchKernelGGL((pool_kernel<uint16_t, 128>), grid, block, 0, st, (const uint16_t*)x0, out0,
-                         (const uint16_t*)x1, out1, g, nitems);
+                         (const uint16_t*)x1, out1, g, nitems, cm1);
     else
       hipLaunchKernelGGL((pool_kernel<uint16_t, 64>), grid, block, 0, st, (const uint16_t*)x0, out0,
-                         (const uint16_t*)x1, out1, g, nitems);
+                         (const uint16_t*)x1, out1, g, nitems, cm1);
   } else {
     if (D == 128)
       hipLaunchKernelGGL((pool_kernel<float, 128>), grid, block, 0, st, (const float*)x0, out0,
-                         (const float*)x1, out1, g, nitems);
+                         (const float*)x1, out1, g, nitems, cm1);
     else
       hipLaunchKernelGGL((pool_kernel<float, 64>), grid, block, 0, st, (const float*)x0, out0,
-                         (const float*)x1, out1, g, nitems);
+                         (const float*)x1, out1, g, nitems, cm1);
   }
   return hipGetLastError();
 }
