@@ -54,11 +54,11 @@ hipError_t summarize(const void* q, const void* k, const vsa_shape* shape, const
     return launch_pool(q, s0, k, s1, shape->dtype, shape->D, dg, BH, st, true);
   }
   if (ps.estimator == VSA_EST_DSA) {
-    *sm = Summaries{s0, nullptr, s1, s2};
-    return launch_extremes(q, s0, nullptr, 1, k, s1, s2, 0, shape->dtype, shape->D, dg, BH, st);
+    *sm = Summaries{s0, nullptr, s1, s2, 1};
+    return launch_extremes(q, s0, nullptr, 1, k, s1, s2, 0, shape->dtype, shape->D, dg, BH, st, true);
   }
-  *sm = Summaries{s0, s1, s2, s3};
-  return launch_extremes(q, s0, s1, 0, k, s2, s3, 0, shape->dtype, shape->D, dg, BH, st);
+  *sm = Summaries{s0, s1, s2, s3, 1};
+  return launch_extremes(q, s0, s1, 0, k, s2, s3, 0, shape->dtype, shape->D, dg, BH, st, true);
 }
 
 }  // namespace

@@ -126,7 +126,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void extremes_kernel(const T* __restrict__ x0, float* __restrict__ omax0,
                                                        float* __restrict__ omin0, int mid0,
                                                        const T* __restrict__ x1, float* __restrict__ omax1,
-                                                       float* __restrict__ omin1, int mid1, DGeo g, int nitems) {
+                                                       float* __restrict__ omin1, int mid1, DGeo g, int nitems,
+                                                       int cm1) {
   constexpr int C = D / 64;
   constexpr int PF = 32;
   constexpr int ROWB = D * (int)sizeof(T);
@@ -177,6 +178,15 @@ __global__ __launch_bounds__(256) void extremes_kernel(const T* __restrict__ x0,
       }
     }
   }
+  if (blockIdx.y && cm1) {   // channel-major max/min: channel d of block j at [bh][d][j]
+    const size_t o = ((size_t)bh * D + lane * C) * g.NB + j;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      omax[o + (size_t)c * g.NB] = mx[c];
+      omin[o + (size_t)c * g.NB] = mn[c];
+    }
+    return;
+  }
   float* oa = omax + (size_t)item * D + lane * C;
   if (mid) {
 #pragma unroll
@@ -191,143 +201,56 @@ __global__ __launch_bounds__(256) void extremes_kernel(const T* __restrict__ x0,
   }
 }
 
-// Scores of RT query blocks (rows i0..i0+RT-1, clamped) against key block j.
-// The query means are wave-uniform, so they come through scalar loads.
-template <int RT>
-__device__ inline void score_column(const float* __restrict__ qrows, const float* __restrict__ kj,
-                                    int D, float (&acc)[RT]) {
-#pragma unroll
-  for (int r = 0; r < RT; ++r) acc[r] = 0.0f;
-  for (int d = 0; d < D; d += 4) {
-    const float4 kv = *reinterpret_cast<const float4*>(kj + d);
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      const float4 qv = *reinterpret_cast<const float4*>(qrows + (size_t)r * D + d);
-      acc[r] = __fadd_rn(acc[r], __fmul_rn(qv.x, kv.x));
-      acc[r] = __fadd_rn(acc[r], __fmul_rn(qv.y, kv.y));
-      acc[r] = __fadd_rn(acc[r], __fmul_rn(qv.z, kv.z));
-      acc[r] = __fadd_rn(acc[r], __fmul_rn(qv.w, kv.w));
-    }
-  }
-}
-
-// Mean scores of RG query rows (qr[x]: D floats each, the same for the whole
-// wave, so they come through scalar loads) against the key block whose
-// channel d is at kj[d * sd]: the same products and the same channel order
-// as score_column, for either key-mean layout.
-template <int RG>
-__device__ inline void mean_column(const float* const (&qr)[RG], const float* __restrict__ kj, size_t sd,
-                                   int D, float (&acc)[RG]) {
+// Scores of RG query blocks against one key block for an estimator (EST 0:
+// mean, 1: DSA, 2: DSA2).  qa[x]/qb[x] are query block x's summaries (mean,
+// or midpoint, or max/min; D floats each, the same for the whole wave, so
+// they come through scalar loads); channel d of the key block's summaries
+// is at ka[d * sd] / kb[d * sd] (mean, or max/min), so either summary
+// layout reads through it.  Channel by channel, in order from +0, the mean
+// adds the rounded product; DSA the larger of the midpoint's two rounded
+// products with the key box corners; DSA2 the largest of the four corner
+// products.
+template <int EST, int RG>
+__device__ inline void est_column(const float* const (&qa)[RG], const float* const (&qb)[RG],
+                                  const float* __restrict__ ka, const float* __restrict__ kb, size_t sd, int D,
+                                  float (&acc)[RG]) {
 #pragma unroll
   for (int x = 0; x < RG; ++x) acc[x] = 0.0f;
-#pragma unroll 4
+#pragma unroll (EST == 2 ? 2 : 4)   // DSA2's second query summary doubles the scalar loads
   for (int d = 0; d < D; d += 4) {
-    const float k0 = kj[(size_t)d * sd], k1 = kj[(size_t)(d + 1) * sd];
-    const float k2 = kj[(size_t)(d + 2) * sd], k3 = kj[(size_t)(d + 3) * sd];
+    float kA[4], kB[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      kA[e] = ka[(size_t)(d + e) * sd];
+      kB[e] = EST != 0 ? kb[(size_t)(d + e) * sd] : 0.0f;
+    }
 #pragma unroll
     for (int x = 0; x < RG; ++x) {
-      const float4 qv = *reinterpret_cast<const float4*>(qr[x] + d);
-      acc[x] = __fadd_rn(acc[x], __fmul_rn(qv.x, k0));
-      acc[x] = __fadd_rn(acc[x], __fmul_rn(qv.y, k1));
-      acc[x] = __fadd_rn(acc[x], __fmul_rn(qv.z, k2));
-      acc[x] = __fadd_rn(acc[x], __fmul_rn(qv.w, k3));
-    }
-  }
-}
-
-// Scores of RT query-block summaries against key block j for an estimator
-// (EST 0: mean, 1: DSA, 2: DSA2).  qa/qb are the query summaries (mean, or
-// midpoint, or max/min), ka/kb the key summaries (mean, or max/min).  DSA
-// adds, channel by channel, the larger of the two rounded products of the
-// midpoint with the key box corners; DSA2 the largest of the four corner
-// products; the sums run over channels in order from +0.
-template <int EST, int RT>
-__device__ inline void est_column(const float* __restrict__ qa, const float* __restrict__ qb,
-                                  const float* __restrict__ ka, const float* __restrict__ kb, int D,
-                                  float (&acc)[RT]) {
-  if constexpr (EST == 0) {
-    score_column<RT>(qa, ka, D, acc);
-  } else {
+      const float4 a4 = *reinterpret_cast<const float4*>(qa[x] + d);
+      const float qA[4] = {a4.x, a4.y, a4.z, a4.w};
+      float qB[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (EST == 2) {
+        const float4 b4 = *reinterpret_cast<const float4*>(qb[x] + d);
+        qB[0] = b4.x;
+        qB[1] = b4.y;
+        qB[2] = b4.z;
+        qB[3] = b4.w;
+      }
 #pragma unroll
-    for (int r = 0; r < RT; ++r) acc[r] = 0.0f;
-    for (int d = 0; d < D; d += 4) {
-      const float4 kA = *reinterpret_cast<const float4*>(ka + d);
-      const float4 kB = *reinterpret_cast<const float4*>(kb + d);
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        const float4 qA = *reinterpret_cast<const float4*>(qa + (size_t)r * D + d);
-        if constexpr (EST == 1) {
-          acc[r] = __fadd_rn(acc[r], fmaxf(__fmul_rn(qA.x, kA.x), __fmul_rn(qA.x, kB.x)));
-          acc[r] = __fadd_rn(acc[r], fmaxf(__fmul_rn(qA.y, kA.y), __fmul_rn(qA.y, kB.y)));
-          acc[r] = __fadd_rn(acc[r], fmaxf(__fmul_rn(qA.z, kA.z), __fmul_rn(qA.z, kB.z)));
-          acc[r] = __fadd_rn(acc[r], fmaxf(__fmul_rn(qA.w, kA.w), __fmul_rn(qA.w, kB.w)));
-        } else {
-          const float4 qB = *reinterpret_cast<const float4*>(qb + (size_t)r * D + d);
-          acc[r] = __fadd_rn(acc[r], fmaxf(fmaxf(__fmul_rn(qA.x, kA.x), __fmul_rn(qA.x, kB.x)),
-                                           fmaxf(__fmul_rn(qB.x, kA.x), __fmul_rn(qB.x, kB.x))));
-          acc[r] = __fadd_rn(acc[r], fmaxf(fmaxf(__fmul_rn(qA.y, kA.y), __fmul_rn(qA.y, kB.y)),
-                                           fmaxf(__fmul_rn(qB.y, kA.y), __fmul_rn(qB.y, kB.y))));
-          acc[r] = __fadd_rn(acc[r], fmaxf(fmaxf(__fmul_rn(qA.z, kA.z), __fmul_rn(qA.z, kB.z)),
-                                           fmaxf(__fmul_rn(qB.z, kA.z), __fmul_rn(qB.z, kB.z))));
-          acc[r] = __fadd_rn(acc[r], fmaxf(fmaxf(__fmul_rn(qA.w, kA.w), __fmul_rn(qA.w, kB.w)),
-                                           fmaxf(__fmul_rn(qB.w, kA.w), __fmul_rn(qB.w, kB.w))));
-        }
+      for (int e = 0; e < 4; ++e) {
+        float t;
+        if constexpr (EST == 0)
+          t = __fmul_rn(qA[e], kA[e]);
+        else if constexpr (EST == 1)
+          t = fmaxf(__fmul_rn(qA[e], kA[e]), __fmul_rn(qA[e], kB[e]));
+        else
+          t = fmaxf(fmaxf(__fmul_rn(qA[e], kA[e]), __fmul_rn(qA[e], kB[e])),
+                    fmaxf(__fmul_rn(qB[e], kA[e]), __fmul_rn(qB[e], kB[e])));
+        acc[x] = __fadd_rn(acc[x], t);
       }
     }
   }
 }
-
-// The box estimators' scores with the RT query summaries staged in LDS
-// (qa_s, qb_s: [RT][D] floats) and the key box read 32 channels at a time,
-// so a column waits for D/32 pairs of loads instead of D/4.  The per-score
-// order is unchanged: channels ascending, each term added on its own.  (The
-// mean estimator keeps est_column: its query means come through scalar
-// loads, which staging in LDS only slows down.)
-template <int EST, int RT>
-__device__ inline void est_column_staged(const float* qa_s, const float* qb_s, const float* __restrict__ ka,
-                                         const float* __restrict__ kb, int D, float (&acc)[RT]) {
-#pragma unroll
-  for (int r = 0; r < RT; ++r) acc[r] = 0.0f;
-  for (int d0 = 0; d0 < D; d0 += 32) {
-    float4 kA[8], kB[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      kA[u] = *reinterpret_cast<const float4*>(ka + d0 + 4 * u);
-      if constexpr (EST != 0) kB[u] = *reinterpret_cast<const float4*>(kb + d0 + 4 * u);
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        const float4 qA = *reinterpret_cast<const float4*>(qa_s + r * D + d0 + 4 * u);
-        if constexpr (EST == 0) {
-          acc[r] = __fadd_rn(acc[r], __fmul_rn(qA.x, kA[u].x));
-          acc[r] = __fadd_rn(acc[r], __fmul_rn(qA.y, kA[u].y));
-          acc[r] = __fadd_rn(acc[r], __fmul_rn(qA.z, kA[u].z));
-          acc[r] = __fadd_rn(acc[r], __fmul_rn(qA.w, kA[u].w));
-        } else if constexpr (EST == 1) {
-          acc[r] = __fadd_rn(acc[r], fmaxf(__fmul_rn(qA.x, kA[u].x), __fmul_rn(qA.x, kB[u].x)));
-          acc[r] = __fadd_rn(acc[r], fmaxf(__fmul_rn(qA.y, kA[u].y), __fmul_rn(qA.y, kB[u].y)));
-          acc[r] = __fadd_rn(acc[r], fmaxf(__fmul_rn(qA.z, kA[u].z), __fmul_rn(qA.z, kB[u].z)));
-          acc[r] = __fadd_rn(acc[r], fmaxf(__fmul_rn(qA.w, kA[u].w), __fmul_rn(qA.w, kB[u].w)));
-        } else {
-          const float4 qB = *reinterpret_cast<const float4*>(qb_s + r * D + d0 + 4 * u);
-          acc[r] = __fadd_rn(acc[r], fmaxf(fmaxf(__fmul_rn(qA.x, kA[u].x), __fmul_rn(qA.x, kB[u].x)),
-                                           fmaxf(__fmul_rn(qB.x, kA[u].x), __fmul_rn(qB.x, kB[u].x))));
-          acc[r] = __fadd_rn(acc[r], fmaxf(fmaxf(__fmul_rn(qA.y, kA[u].y), __fmul_rn(qA.y, kB[u].y)),
-                                           fmaxf(__fmul_rn(qB.y, kA[u].y), __fmul_rn(qB.y, kB[u].y))));
-          acc[r] = __fadd_rn(acc[r], fmaxf(fmaxf(__fmul_rn(qA.z, kA[u].z), __fmul_rn(qA.z, kB[u].z)),
-                                           fmaxf(__fmul_rn(qB.z, kA[u].z), __fmul_rn(qB.z, kB[u].z))));
-          acc[r] = __fadd_rn(acc[r], fmaxf(fmaxf(__fmul_rn(qA.w, kA[u].w), __fmul_rn(qA.w, kB[u].w)),
-                                           fmaxf(__fmul_rn(qB.w, kA[u].w), __fmul_rn(qB.w, kB[u].w))));
-        }
-      }
-    }
-  }
-}
-
-// Floats of LDS before the staged query summaries (16-byte aligned).
-__host__ __device__ inline int staged_q_offset(int RT, int NB) { return (RT * NB + 3) & ~3; }
 
 // Orderable key of a score: larger float -> larger key; -0 and +0 map to
 // the same key, so they tie (and the lower block id wins).
@@ -545,7 +468,7 @@ __global__ __launch_bounds__(256) void score_select_kernel(
     Summaries sm, DGeo g, int D, int heads,
     SelectArgs sa, int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
     int32_t* __restrict__ counts, uint64_t* __restrict__ bits) {
-  extern __shared__ uint32_t smem[];   // [RT][NB] keys, then (RT >= 2) the staged query summaries
+  extern __shared__ uint32_t smem[];   // [RT][NB] keys
   const int NB = g.NB;
   const int bh = blockIdx.y;
   const int i0 = blockIdx.x * RT;
@@ -569,11 +492,12 @@ __global__ __launch_bounds__(256) void score_select_kernel(
   } else if (kind == 2) {
     for (int r = 0; r < rows_here; ++r)
       for (int j = tid; j < NB; j += 256) smem[r * NB + j] = 0x80000000u;
-  } else if (EST == 0) {
-    // Mean scores.  A task is RG rows x 64 consecutive key blocks (lane =
-    // key block) and the tasks are dealt evenly to the waves; with the
-    // channel-major key means every load of a channel is 256 contiguous
-    // bytes.  Rows past rows_here read the last row and are not stored.
+  } else {
+    // Estimator scores.  A task is RG rows x 64 consecutive key blocks
+    // (lane = key block) and the tasks are dealt evenly to the waves; with
+    // the planner's channel-major key summaries every load of a channel is
+    // 256 contiguous bytes.  Rows past rows_here read the last row and are
+    // not stored.
     constexpr int RG = RT < 4 ? RT : 4;
     const int wv = uniform_i(wave);
     const int chunks = (NB + 63) >> 6;
@@ -582,47 +506,21 @@ __global__ __launch_bounds__(256) void score_select_kernel(
     for (int task = wv; task < tasks; task += 4) {
       const int rg = task / chunks, ch = task - rg * chunks;
       const int j = ch * 64 + lane;
-      const float* qr[RG];
+      const float* qra[RG];
+      const float* qrb[RG];
 #pragma unroll
-      for (int x = 0; x < RG; ++x) qr[x] = qa + (size_t)(i0 + min(rg * RG + x, rows_here - 1)) * D;
+      for (int x = 0; x < RG; ++x) {
+        const size_t qi = (size_t)(i0 + min(rg * RG + x, rows_here - 1)) * D;
+        qra[x] = qa + qi;
+        qrb[x] = (EST == 2 ? qb : qa) + qi;
+      }
+      const size_t kj = (size_t)min(j, NB - 1) * sj;
       float acc[RG];
-      mean_column<RG>(qr, ka + (size_t)min(j, NB - 1) * sj, sd, D, acc);
+      est_column<EST, RG>(qra, qrb, ka + kj, (EST != 0 ? kb : ka) + kj, sd, D, acc);
       if (j < NB) {
 #pragma unroll
         for (int x = 0; x < RG; ++x)
           if (rg * RG + x < rows_here) smem[(rg * RG + x) * NB + j] = order_key(acc[x]);
-      }
-    }
-  } else if (RT >= 2 && rows_here == RT) {
-    float* qa_s = reinterpret_cast<float*>(smem) + staged_q_offset(RT, NB);
-    float* qb_s = qa_s + RT * D;
-    for (int x = tid; x < RT * D; x += 256) {
-      qa_s[x] = qa[(size_t)i0 * D + x];
-      if constexpr (EST == 2) qb_s[x] = qb[(size_t)i0 * D + x];
-    }
-    __syncthreads();
-    for (int j = tid; j < NB; j += 256) {
-      float acc[RT];
-      est_column_staged<EST, RT>(qa_s, qb_s, ka + (size_t)j * D, kb + (EST != 0 ? (size_t)j * D : 0), D, acc);
-#pragma unroll
-      for (int r = 0; r < RT; ++r) smem[r * NB + j] = order_key(acc[r]);
-    }
-  } else if (rows_here == RT) {
-    for (int j = tid; j < NB; j += 256) {
-      float acc[RT];
-      est_column<EST, RT>(qa + (size_t)i0 * D, qb + (EST == 2 ? (size_t)i0 * D : 0), ka + (size_t)j * D,
-                          kb + (EST != 0 ? (size_t)j * D : 0), D, acc);
-#pragma unroll
-      for (int r = 0; r < RT; ++r) smem[r * NB + j] = order_key(acc[r]);
-    }
-  } else {
-    for (int j = tid; j < NB; j += 256) {
-      for (int r = 0; r < rows_here; ++r) {
-        float acc[1];
-        const size_t qi = (size_t)(i0 + r) * D;
-        est_column<EST, 1>(qa + qi, qb + (EST == 2 ? qi : 0), ka + (size_t)j * D,
-                           kb + (EST != 0 ? (size_t)j * D : 0), D, acc);
-        smem[r * NB + j] = order_key(acc[0]);
       }
     }
   }
@@ -638,7 +536,13 @@ __global__ __launch_bounds__(256) void score_select_kernel(
     uint32_t thr;
     int need;
     if constexpr (TOPP) {
-      if (NB <= 64 * 8)
+      // The fewest register chunks that hold the row; the chunks left out
+      // would only add +0 to each lane's non-negative partial sums.
+      if (NB <= 64 * 4)
+        topp_cut_regs<4>(keys, NB, lane, sa.p[h], sa.scale, thr, need);
+      else if (NB <= 64 * 6)
+        topp_cut_regs<6>(keys, NB, lane, sa.p[h], sa.scale, thr, need);
+      else if (NB <= 64 * 8)
         topp_cut_regs<8>(keys, NB, lane, sa.p[h], sa.scale, thr, need);
       else
         topp_cut_lds(keys, NB, lane, sa.p[h], sa.scale, thr, need);
@@ -734,16 +638,13 @@ __global__ __launch_bounds__(256) void scores_kernel(Summaries sm, float* __rest
   const int i = blockIdx.x;
   const size_t head = (size_t)bh * NB * D;
   const size_t qi = head + (size_t)i * D;
+  const size_t sj = sm.kt ? 1 : (size_t)D, sd = sm.kt ? (size_t)NB : 1;
+  const float* qra[1] = {sm.qa + qi};
+  const float* qrb[1] = {(EST == 2 ? sm.qb : sm.qa) + qi};
   for (int j = threadIdx.x; j < NB; j += 256) {
     float acc[1];
-    const size_t kj = head + (size_t)j * D;
-    if constexpr (EST == 0) {
-      const float* qr[1] = {sm.qa + qi};
-      mean_column<1>(qr, sm.ka + (sm.kt ? head + j : kj), sm.kt ? (size_t)NB : 1, D, acc);
-    } else {
-      est_column<EST, 1>(sm.qa + qi, EST == 2 ? sm.qb + qi : nullptr, sm.ka + kj, EST != 0 ? sm.kb + kj : nullptr,
-                         D, acc);
-    }
+    const size_t kj = head + (size_t)j * sj;
+    est_column<EST, 1>(qra, qrb, sm.ka + kj, (EST != 0 ? sm.kb : sm.ka) + kj, sd, D, acc);
     out[((size_t)bh * NB + i) * NB + j] = acc[0];
   }
 }
@@ -774,18 +675,13 @@ hipError_t launch_pool(const void* x0, float* out0, const void* x1, float* out1,
   return hipGetLastError();
 }
 
-// LDS of a workgroup with RT rows: RT rows of NB uint32 keys, and for the
-// box estimators with RT >= 2 the staged query summaries (RT x D floats, two
-// sets for DSA2).
-size_t select_lds_bytes(int RT, int NB, int D, int est) {
-  if (est == 0 || RT < 2) return (size_t)RT * NB * 4;
-  return (size_t)staged_q_offset(RT, NB) * 4 + (size_t)RT * D * 4 * (est == 2 ? 2 : 1);
-}
+// LDS of a workgroup with RT rows: RT rows of NB uint32 keys.
+size_t select_lds_bytes(int RT, int NB) { return (size_t)RT * NB * 4; }
 
 // Rows per workgroup: the most rows whose LDS fits in 64 KiB.
-int select_rows_per_block(int NB, int D, int est) {
+int select_rows_per_block(int NB) {
   for (int RT = 8; RT >= 2; RT >>= 1)
-    if (select_lds_bytes(RT, NB, D, est) <= 65536) return RT;
+    if (select_lds_bytes(RT, NB) <= 65536) return RT;
   return 1;
 }
 
@@ -814,9 +710,9 @@ void launch_score_select_e(int RT, dim3 grid, dim3 block, size_t lds, hipStream_
 hipError_t launch_score_select(const Summaries& sm, int est, const DGeo& g, int D, int heads, int BH,
                                const SelectArgs& sa, int32_t* row_ptr, int32_t* col_idx, int32_t* counts,
                                uint64_t* bits, hipStream_t st) {
-  const int RT = select_rows_per_block(g.NB, D, est);
+  const int RT = select_rows_per_block(g.NB);
   dim3 grid((g.NB + RT - 1) / RT, BH), block(256);
-  const size_t lds = select_lds_bytes(RT, g.NB, D, est);
+  const size_t lds = select_lds_bytes(RT, g.NB);
   if (est == 1)
     launch_score_select_e<1>(RT, grid, block, lds, st, sm, g, D, heads, sa, row_ptr, col_idx, counts, bits);
   else if (est == 2)
@@ -847,23 +743,25 @@ hipError_t launch_scores(const Summaries& sm, int est, float* out, int NB, int D
 }
 
 hipError_t launch_extremes(const void* x0, float* max0, float* min0, int mid0, const void* x1, float* max1,
-                           float* min1, int mid1, int dtype, int D, const DGeo& g, int BH, hipStream_t st) {
+                           float* min1, int mid1, int dtype, int D, const DGeo& g, int BH, hipStream_t st,
+                           bool out1_channel_major) {
   const int nitems = BH * g.NB;
+  const int cm1 = out1_channel_major && !mid1 ? 1 : 0;
   dim3 grid((nitems + 3) / 4, x1 ? 2 : 1), block(256);
   if (dtype == 0) {
     if (D == 128)
       hipLaunchKernelGGL((extremes_kernel<uint16_t, 128>), grid, block, 0, st, (const uint16_t*)x0, max0, min0, mid0,
-                         (const uint16_t*)x1, max1, min1, mid1, g, nitems);
+                         (const uint16_t*)x1, max1, min1, mid1, g, nitems, cm1);
     else
       hipLaunchKernelGGL((extremes_kernel<uint16_t, 64>), grid, block, 0, st, (const uint16_t*)x0, max0, min0, mid0,
-                         (const uint16_t*)x1, max1, min1, mid1, g, nitems);
+                         (const uint16_t*)x1, max1, min1, mid1, g, nitems, cm1);
   } else {
     if (D == 128)
       hipLaunchKernelGGL((extremes_kernel<float, 128>), grid, block, 0, st, (const float*)x0, max0, min0, mid0,
-                         (const float*)x1, max1, min1, mid1, g, nitems);
+                         (const float*)x1, max1, min1, mid1, g, nitems, cm1);
     else
       hipLaunchKernelGGL((extremes_kernel<float, 64>), grid, block, 0, st, (const float*)x0, max0, min0, mid0,
-                         (const float*)x1, max1, min1, mid1, g, nitems);
+                         (const float*)x1, max1, min1, mid1, g, nitems, cm1);
   }
   return hipGetLastError();
 }

@@ -39,7 +39,7 @@ struct SchemeArgs {
 // Block summaries an estimator reads, each float32 [BH][NB][D]: mean: qa =
 // query means, ka = key means; DSA: qa = query midpoints, ka/kb = key
 // max/min; DSA2: qa/qb = query max/min, ka/kb = key max/min.  With kt set
-// the key means are channel-major instead, [BH][D][NB], so that a wave
+// the key summaries are channel-major instead, [BH][D][NB], so that a wave
 // reading one channel of 64 consecutive key blocks touches 256 contiguous
 // bytes (the planner's own layout; callers' centroids stay [BH][NB][D]).
 struct Summaries {
@@ -54,9 +54,11 @@ struct Summaries {
 // ([BH][NB][D], or [BH][D][NB] for out1 when out1_channel_major).
 hipError_t launch_pool(const void* x0, float* out0, const void* x1, float* out1, int dtype, int D,
                        const DGeo& g, int BH, hipStream_t st, bool out1_channel_major = false);
-// Block max/min of x0 (or, with mid0, the midpoint into max0) and of x1.
+// Block max/min of x0 (or, with mid0, the midpoint into max0) and of x1
+// (channel-major when out1_channel_major and not mid1).
 hipError_t launch_extremes(const void* x0, float* max0, float* min0, int mid0, const void* x1, float* max1,
-                           float* min1, int mid1, int dtype, int D, const DGeo& g, int BH, hipStream_t st);
+                           float* min1, int mid1, int dtype, int D, const DGeo& g, int BH, hipStream_t st,
+                           bool out1_channel_major = false);
 // est: 0 mean, 1 DSA, 2 DSA2 (vsa_estimator).
 hipError_t launch_score_select(const Summaries& sm, int est, const DGeo& g, int D, int heads, int BH,
                                const SelectArgs& sa, int32_t* row_ptr, int32_t* col_idx, int32_t* counts,

@@ -136,6 +136,25 @@ def test_small_select_parity(vsa, case):
     _say(f"[gpu]   ok rows={rows} band={band} nnz={idx.nnz()} max-abs {err.max():.2e}")
 
 
+# Rows of NB blocks keep their keys in 4, 6 or 8 register chunks of 64 (the
+# fewest that hold the row) and longer rows in LDS: each width at its edges.
+WIDTHS = [(256, (1, 32, 32)), (257, (1, 2, 514)), (384, (1, 32, 48)), (385, (1, 10, 154)),
+          (512, (1, 32, 64)), (513, (1, 54, 38))]
+
+
+@pytest.mark.parametrize("mode,val", [("topk", 0.3), ("topp", 0.5)])
+@pytest.mark.parametrize("nb,grid", WIDTHS, ids=[f"nb{n}" for n, _ in WIDTHS])
+def test_register_chunk_widths(vsa, nb, grid, mode, val):
+    w = W.custom(f"cw{nb}", 1, 2, 64, grid, (1, 2, 2), "bf16", 0.5, -1, "smooth")
+    _say(f"[gpu] select chunk widths NB={nb}: {mode} {val} grid={grid}")
+    inp = W.generate(w, seed=12)
+    _, idx, g, S = _plan_both(vsa, w, inp, mode, [val], -1, 1, None)
+    assert g.NB == nb
+    grp, gci = _index_np(idx)
+    (rows, band, _), _ = check_index(grp, gci, S, g, mode, [val], -1, 1, _scale(w, None))
+    _say(f"[gpu]   ok rows={rows} band={band} nnz={idx.nnz()}")
+
+
 def test_topp_uniform_ties(vsa):
     """Q == 0 makes every score 0: Top-P keeps ceil(p * NB) blocks, the
     lowest ids (p * NB = 4.8 here, far from an integer)."""
