@@ -168,6 +168,51 @@ def time_select(vsa, lib, _lib, q, k, v, o, w, mode, val, sink, stream, sizes, e
             "row_len_min_max": [int(lens.min()), int(lens.max())]}
 
 
+def time_layout(vsa, lib, _lib, x, w, stream, reps=20):
+    """Standalone permute (raster -> blocked, zero pad rows) and unpermute of
+    one tensor into preallocated buffers, timed with events on the stream;
+    algorithmic bytes = one read of the source and one write of the
+    destination (raster N*D plus blocked NB*bt*bh*bw*D elements)."""
+    import ctypes
+
+    import torch
+    s = vsa._shape_of(x, w.grid, w.block)
+    nb = int(np.prod([-(-int(n) // int(b)) for n, b in zip(w.grid, w.block)]))
+    P = s.bt * s.bh * s.bw
+    xb = torch.empty((s.B, s.heads, nb, P, s.D), dtype=x.dtype, device=x.device)
+    xr = torch.empty_like(x)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    xp, bp, rp = (ctypes.c_void_p(t.data_ptr()) for t in (x, xb, xr))
+
+    def perm():
+        _lib.check(lib.vsa_permute(xp, ctypes.byref(s), bp, sp), "vsa_permute")
+
+    def unperm():
+        _lib.check(lib.vsa_unpermute(bp, ctypes.byref(s), rp, sp), "vsa_unpermute")
+
+    for _ in range(3):
+        perm(); unperm()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record(stream)
+    for _ in range(reps):
+        perm()
+    e[1].record(stream)
+    for _ in range(reps):
+        unperm()
+    e[2].record(stream)
+    torch.cuda.synchronize()
+    pm, um = e[0].elapsed_time(e[1]) / reps, e[1].elapsed_time(e[2]) / reps
+    nbytes = (x.numel() + xb.numel()) * x.element_size()
+    return {"tensor": "k", "permute_ms": round(pm, 4), "unpermute_ms": round(um, 4),
+            "algorithmic_bytes": int(nbytes),
+            "permute_GB_per_s": round(nbytes / (pm * 1e-3) / 1e9, 1),
+            "unpermute_GB_per_s": round(nbytes / (um * 1e-3) / 1e9, 1),
+            "hbm_frac_permute": round(nbytes / (pm * 1e-3) / 8e12, 4),
+            "hbm_frac_unpermute": round(nbytes / (um * 1e-3) / 8e12, 4),
+            "roundtrip_identical": bool(torch.equal(xr, x))}
+
+
 def time_mixed(vsa, lib, _lib, q, k, v, o, w, stream, sizes, reps=20):
     """A mixed per-head plan on the bench shape (dense, static, dynamic heads
     with windows; a seeded static ranking table), timed like time_select."""
@@ -391,6 +436,10 @@ def main():
             for est, mode, val, sink in (("mean", "topp", 0.25, 2), ("mean", "topk", 0.2, 2),
                                          ("dsa", "topk", 0.2, 0), ("dsa2", "topk", 0.2, 0))]
         result["mixed_plan"] = time_mixed(vsa, lib, _lib, q, k, v, o, w, stream, sizes)
+        # Standalone layout kernels (the attention kernel gathers from and
+        # stores to raster order itself; these serve callers that want the
+        # blocked layout), against the HBM roofline.
+        result["layout"] = time_layout(vsa, lib, _lib, k, w, stream)
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inp, w, rp, ci, sizes, flops, a.cpu_budget)
