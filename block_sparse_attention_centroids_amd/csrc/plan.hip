@@ -22,183 +22,81 @@
 namespace vsa {
 
 // ---------------------------------------------------------------------------
-// Block means.  One wave per (tensor, row bh, block j); lane c owns D/64
-// consecutive channels and walks the block's tokens in block order.  Token
-// offsets are stepped on the scalar unit and fed to the buffer loads as a
-// scalar offset, so a wave keeps PF token loads in flight; the adds stay in
-// token order.  Loads past the block's last token read out of range and
-// return +0, and adding +0 leaves a sum that started at +0 unchanged.
+// Block summaries (means for the mean estimator, max/min or the midpoint for
+// the box estimators).  One workgroup per (tensor, row bh, block j).  The
+// workgroup copies the block's n tokens into LDS in 16-byte pieces (every
+// load coalesced, as in the layout kernels); then thread c walks channel c
+// over the tokens in block order.  The mean adds them one by one from +0
+// and divides once (correctly rounded); max and min are exact.  The query
+// midpoint is fl(fl(max + min) * 0.5).  With cm1 the second tensor's
+// summaries go channel-major ([BH][D][NB]).
 // ---------------------------------------------------------------------------
 __device__ inline int uniform_i(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-__device__ inline __amdgpu_buffer_rsrc_t plan_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0,
-                                           (int)bytes, 0x00020000);
-}
-
-// One token's C channels for this lane, as float (bf16 widens exactly).
-template <typename T, int C>
-__device__ inline void load_token(__amdgpu_buffer_rsrc_t rs, int voff, int soff, float (&v)[C]) {
-  if constexpr (sizeof(T) == 2 && C == 2) {
-    const uint32_t two = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0);
-    v[0] = bf16_lo(two);
-    v[1] = bf16_hi(two);
-  } else if constexpr (sizeof(T) == 2) {
-    v[0] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rs, voff, soff, 0));
-  } else if constexpr (C == 2) {
-    const auto two = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0);
-    v[0] = __uint_as_float(two[0]);
-    v[1] = __uint_as_float(two[1]);
-  } else {
-    v[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0));
-  }
-}
-
-template <typename T, int D>
-__global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ x0, float* __restrict__ out0,
-                                                   const T* __restrict__ x1, float* __restrict__ out1,
-                                                   DGeo g, int nitems, int cm1) {
-  constexpr int C = D / 64;   // channels per lane
-  constexpr int PF = 32;      // token loads in flight per wave
+template <typename T, int D, bool EXT>
+__global__ __launch_bounds__(256) void summary_kernel(const T* __restrict__ x0, float* __restrict__ oa0,
+                                                      float* __restrict__ ob0, int mid0,
+                                                      const T* __restrict__ x1, float* __restrict__ oa1,
+                                                      float* __restrict__ ob1, int mid1, DGeo g, int cm1) {
   constexpr int ROWB = D * (int)sizeof(T);
-  const int wave = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + wave;
-  if (item >= nitems) return;
-  const T* x = blockIdx.y ? x1 : x0;
-  float* out = blockIdx.y ? out1 : out0;
+  constexpr int PIECES = ROWB / 16;
+  extern __shared__ uint4 stage16[];   // the block's tokens, [n][D] of T (room for 128)
+  const T* stage = reinterpret_cast<const T*>(stage16);
+  const int item = blockIdx.x;         // bh * NB + j
+  const bool second = blockIdx.y != 0;
+  const T* x = second ? x1 : x0;
+  float* oa = second ? oa1 : oa0;
+  float* ob = second ? ob1 : ob0;
+  const int mid = second ? mid1 : mid0;
   const int bh = item / g.NB, j = item - bh * g.NB;
   const Box b = block_box(g, j);
-  const int n = uniform_i(b.n());
-  const __amdgpu_buffer_rsrc_t rs = plan_rsrc(x + (size_t)bh * g.N * D, (uint32_t)g.N * ROWB);
-  const int voff = lane * C * (int)sizeof(T);
-  // Scalar token cursor: byte offset of token u of the block, and its (h, w)
-  // position inside the box for stepping.
-  int soff = uniform_i(((b.t0 * g.H + b.h0) * g.W + b.w0) * ROWB);
-  int uh = 0, uw = 0;
-  const int ew = uniform_i(b.ew), eh = uniform_i(b.eh);
-  const int wrap_w = uniform_i((g.W - b.ew) * ROWB), wrap_h = uniform_i((g.H - b.eh) * g.W * ROWB);
-  float acc[C];
+  const int n = b.n();
+  TokenMap map;
+  map.init(g, b);
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(x) + (size_t)bh * g.N * ROWB;
+  // Every piece a thread copies is loaded before any is stored, so the
+  // loads are all in flight together.  Loads and stores are unconditional,
+  // so no branch splits them: a slot past the block's last piece re-reads
+  // that piece into LDS sized for the largest block (128 tokens), where the
+  // channel walk below never reads it.
+  constexpr int MAXIT = (VSA_MAX_BLOCK_TOKENS * PIECES + 255) / 256;
+  const int npieces = n * PIECES;
+  uint4 piece[MAXIT];
 #pragma unroll
-  for (int c = 0; c < C; ++c) acc[c] = 0.0f;
-  for (int u0 = 0; u0 < n; u0 += PF) {
-    float v[PF][C];
-#pragma unroll
-    for (int e = 0; e < PF; ++e) {
-      load_token<T, C>(rs, voff, u0 + e < n ? soff : (int)0x80000000, v[e]);
-      // step to the next token of the box (row-major t, h, w)
-      soff += ROWB;
-      if (++uw == ew) {
-        uw = 0;
-        soff += wrap_w;
-        if (++uh == eh) {
-          uh = 0;
-          soff += wrap_h;
-        }
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < PF; ++e)
-#pragma unroll
-      for (int c = 0; c < C; ++c) acc[c] = __fadd_rn(acc[c], v[e][c]);
+  for (int it = 0; it < MAXIT; ++it) {
+    const int idx = min((int)threadIdx.x + it * 256, npieces - 1);
+    const int u = idx / PIECES, p = idx - u * PIECES;
+    piece[it] = *reinterpret_cast<const uint4*>(src + (size_t)map(u) * ROWB + p * 16);
   }
-  if (blockIdx.y && cm1) {   // channel-major: channel d of block j at [bh][d][j]
-    float* o = out + ((size_t)bh * D + lane * C) * g.NB + j;
 #pragma unroll
-    for (int c = 0; c < C; ++c) o[(size_t)c * g.NB] = __fdiv_rn(acc[c], (float)n);
+  for (int it = 0; it < MAXIT; ++it) stage16[threadIdx.x + it * 256] = piece[it];
+  __syncthreads();
+  const int c = threadIdx.x;
+  if (c >= D) return;
+  auto val = [&](int u) {
+    if constexpr (sizeof(T) == 2)
+      return bf16_to_f32(stage[u * D + c]);
+    else
+      return stage[u * D + c];
+  };
+  float ra, rb = 0.0f;
+  if constexpr (!EXT) {
+    float acc = 0.0f;
+    for (int u = 0; u < n; ++u) acc = __fadd_rn(acc, val(u));
+    ra = __fdiv_rn(acc, (float)n);
   } else {
-    float* o = out + (size_t)item * D + lane * C;
-#pragma unroll
-    for (int c = 0; c < C; ++c) o[c] = __fdiv_rn(acc[c], (float)n);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Block extremes (the max/min summarizer).  Same walk as pool_kernel; a
-// slot past the block's last token re-reads the block's first token, which
-// leaves max and min unchanged, so the reduction needs no predicate.  For a
-// tensor with `mid` set the query midpoint fl(fl(max + min) * 0.5) goes to
-// omax and omin is not written.  max and min are exact.
-// ---------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__(256) void extremes_kernel(const T* __restrict__ x0, float* __restrict__ omax0,
-                                                       float* __restrict__ omin0, int mid0,
-                                                       const T* __restrict__ x1, float* __restrict__ omax1,
-                                                       float* __restrict__ omin1, int mid1, DGeo g, int nitems,
-                                                       int cm1) {
-  constexpr int C = D / 64;
-  constexpr int PF = 32;
-  constexpr int ROWB = D * (int)sizeof(T);
-  const int wave = uniform_i(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + wave;
-  if (item >= nitems) return;
-  const T* x = blockIdx.y ? x1 : x0;
-  float* omax = blockIdx.y ? omax1 : omax0;
-  float* omin = blockIdx.y ? omin1 : omin0;
-  const int mid = blockIdx.y ? mid1 : mid0;
-  const int bh = item / g.NB, j = item - bh * g.NB;
-  const Box b = block_box(g, j);
-  const int n = uniform_i(b.n());
-  const __amdgpu_buffer_rsrc_t rs = plan_rsrc(x + (size_t)bh * g.N * D, (uint32_t)g.N * ROWB);
-  const int voff = lane * C * (int)sizeof(T);
-  const int soff0 = uniform_i(((b.t0 * g.H + b.h0) * g.W + b.w0) * ROWB);
-  int soff = soff0;
-  int uh = 0, uw = 0;
-  const int ew = uniform_i(b.ew), eh = uniform_i(b.eh);
-  const int wrap_w = uniform_i((g.W - b.ew) * ROWB), wrap_h = uniform_i((g.H - b.eh) * g.W * ROWB);
-  float mx[C], mn[C];
-#pragma unroll
-  for (int c = 0; c < C; ++c) {
-    mx[c] = -INFINITY;
-    mn[c] = INFINITY;
-  }
-  for (int u0 = 0; u0 < n; u0 += PF) {
-    float v[PF][C];
-#pragma unroll
-    for (int e = 0; e < PF; ++e) {
-      load_token<T, C>(rs, voff, u0 + e < n ? soff : soff0, v[e]);
-      soff += ROWB;
-      if (++uw == ew) {
-        uw = 0;
-        soff += wrap_w;
-        if (++uh == eh) {
-          uh = 0;
-          soff += wrap_h;
-        }
-      }
+    float mx = -INFINITY, mn = INFINITY;
+    for (int u = 0; u < n; ++u) {
+      const float v = val(u);
+      mx = fmaxf(mx, v);
+      mn = fminf(mn, v);
     }
-#pragma unroll
-    for (int e = 0; e < PF; ++e) {
-#pragma unroll
-      for (int c = 0; c < C; ++c) {
-        mx[c] = fmaxf(mx[c], v[e][c]);
-        mn[c] = fminf(mn[c], v[e][c]);
-      }
-    }
+    ra = mid ? __fmul_rn(__fadd_rn(mx, mn), 0.5f) : mx;
+    rb = mn;
   }
-  if (blockIdx.y && cm1) {   // channel-major max/min: channel d of block j at [bh][d][j]
-    const size_t o = ((size_t)bh * D + lane * C) * g.NB + j;
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      omax[o + (size_t)c * g.NB] = mx[c];
-      omin[o + (size_t)c * g.NB] = mn[c];
-    }
-    return;
-  }
-  float* oa = omax + (size_t)item * D + lane * C;
-  if (mid) {
-#pragma unroll
-    for (int c = 0; c < C; ++c) oa[c] = __fmul_rn(__fadd_rn(mx[c], mn[c]), 0.5f);
-  } else {
-    float* ob = omin + (size_t)item * D + lane * C;
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      oa[c] = mx[c];
-      ob[c] = mn[c];
-    }
-  }
+  const size_t o = (second && cm1) ? ((size_t)bh * D + c) * g.NB + j : (size_t)item * D + c;
+  oa[o] = ra;
+  if (EXT && !mid) ob[o] = rb;
 }
 
 // Scores of RG query blocks against one key block for an estimator (EST 0:
@@ -652,27 +550,40 @@ __global__ __launch_bounds__(256) void scores_kernel(Summaries sm, float* __rest
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_pool(const void* x0, float* out0, const void* x1, float* out1, int dtype, int D,
-                       const DGeo& g, int BH, hipStream_t st, bool out1_channel_major) {
-  const int nitems = BH * g.NB;
-  const int cm1 = out1_channel_major ? 1 : 0;
-  dim3 grid((nitems + 3) / 4, x1 ? 2 : 1), block(256);
+template <bool EXT>
+hipError_t launch_summary(const void* x0, float* a0, float* b0, int mid0, const void* x1, float* a1, float* b1,
+                          int mid1, int dtype, int D, const DGeo& g, int BH, hipStream_t st, int cm1) {
+  dim3 grid((unsigned)(BH * g.NB), x1 ? 2 : 1), block(256);
+  const size_t lds = (size_t)VSA_MAX_BLOCK_TOKENS * D * (dtype == 0 ? 2 : 4);   // every slot the copy writes
   if (dtype == 0) {
     if (D == 128)
-      hipLaunchKernelGGL((pool_kernel<uint16_t, 128>), grid, block, 0, st, (const uint16_t*)x0, out0,
-                         (const uint16_t*)x1, out1, g, nitems, cm1);
+      hipLaunchKernelGGL((summary_kernel<uint16_t, 128, EXT>), grid, block, lds, st, (const uint16_t*)x0, a0, b0,
+                         mid0, (const uint16_t*)x1, a1, b1, mid1, g, cm1);
     else
-      hipLaunchKernelGGL((pool_kernel<uint16_t, 64>), grid, block, 0, st, (const uint16_t*)x0, out0,
-                         (const uint16_t*)x1, out1, g, nitems, cm1);
+      hipLaunchKernelGGL((summary_kernel<uint16_t, 64, EXT>), grid, block, lds, st, (const uint16_t*)x0, a0, b0,
+                         mid0, (const uint16_t*)x1, a1, b1, mid1, g, cm1);
   } else {
     if (D == 128)
-      hipLaunchKernelGGL((pool_kernel<float, 128>), grid, block, 0, st, (const float*)x0, out0,
-                         (const float*)x1, out1, g, nitems, cm1);
+      hipLaunchKernelGGL((summary_kernel<float, 128, EXT>), grid, block, lds, st, (const float*)x0, a0, b0, mid0,
+                         (const float*)x1, a1, b1, mid1, g, cm1);
     else
-      hipLaunchKernelGGL((pool_kernel<float, 64>), grid, block, 0, st, (const float*)x0, out0,
-                         (const float*)x1, out1, g, nitems, cm1);
+      hipLaunchKernelGGL((summary_kernel<float, 64, EXT>), grid, block, lds, st, (const float*)x0, a0, b0, mid0,
+                         (const float*)x1, a1, b1, mid1, g, cm1);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_pool(const void* x0, float* out0, const void* x1, float* out1, int dtype, int D,
+                       const DGeo& g, int BH, hipStream_t st, bool out1_channel_major) {
+  return launch_summary<false>(x0, out0, nullptr, 0, x1, out1, nullptr, 0, dtype, D, g, BH, st,
+                               out1_channel_major ? 1 : 0);
+}
+
+hipError_t launch_extremes(const void* x0, float* max0, float* min0, int mid0, const void* x1, float* max1,
+                           float* min1, int mid1, int dtype, int D, const DGeo& g, int BH, hipStream_t st,
+                           bool out1_channel_major) {
+  return launch_summary<true>(x0, max0, min0, mid0, x1, max1, min1, mid1, dtype, D, g, BH, st,
+                              out1_channel_major && !mid1 ? 1 : 0);
 }
 
 // LDS of a workgroup with RT rows: RT rows of NB uint32 keys.
@@ -742,28 +653,5 @@ hipError_t launch_scores(const Summaries& sm, int est, float* out, int NB, int D
   return hipGetLastError();
 }
 
-hipError_t launch_extremes(const void* x0, float* max0, float* min0, int mid0, const void* x1, float* max1,
-                           float* min1, int mid1, int dtype, int D, const DGeo& g, int BH, hipStream_t st,
-                           bool out1_channel_major) {
-  const int nitems = BH * g.NB;
-  const int cm1 = out1_channel_major && !mid1 ? 1 : 0;
-  dim3 grid((nitems + 3) / 4, x1 ? 2 : 1), block(256);
-  if (dtype == 0) {
-    if (D == 128)
-      hipLaunchKernelGGL((extremes_kernel<uint16_t, 128>), grid, block, 0, st, (const uint16_t*)x0, max0, min0, mid0,
-                         (const uint16_t*)x1, max1, min1, mid1, g, nitems, cm1);
-    else
-      hipLaunchKernelGGL((extremes_kernel<uint16_t, 64>), grid, block, 0, st, (const uint16_t*)x0, max0, min0, mid0,
-                         (const uint16_t*)x1, max1, min1, mid1, g, nitems, cm1);
-  } else {
-    if (D == 128)
-      hipLaunchKernelGGL((extremes_kernel<float, 128>), grid, block, 0, st, (const float*)x0, max0, min0, mid0,
-                         (const float*)x1, max1, min1, mid1, g, nitems, cm1);
-    else
-      hipLaunchKernelGGL((extremes_kernel<float, 64>), grid, block, 0, st, (const float*)x0, max0, min0, mid0,
-                         (const float*)x1, max1, min1, mid1, g, nitems, cm1);
-  }
-  return hipGetLastError();
-}
 
 }  // namespace vsa
