@@ -658,7 +658,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
 // ---------------------------------------------------------------------------
 // float32 path: one thread per query token, 32-key tiles staged in LDS,
-// float32 dot products and an exact-exp online softmax.
+// float32 dot products and an exact-exp online softmax updated once per
+// group of keys.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(128) void attn_f32_kernel(
@@ -666,8 +667,10 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
     float* __restrict__ o, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     DGeo g, float scale) {
   constexpr int TK = 32;
-  __shared__ float Ks[TK][D + 1];
-  __shared__ float Vs[TK][D];
+  constexpr int SK = D == 64 ? 16 : 4;   // keys per score group (registers: q, o and the group's scores)
+  static_assert(TK % SK == 0, "a score group must not run past the tile");
+  __shared__ __attribute__((aligned(16))) float Ks[TK][D];   // every thread reads the same element: broadcasts
+  __shared__ __attribute__((aligned(16))) float Vs[TK][D];
   const int tid = threadIdx.x;
   const int bh = blockIdx.x / g.NB, i = blockIdx.x - bh * g.NB;
   const Box bi = block_box(g, i);
@@ -693,25 +696,64 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
     kmap.init(g, bj);
     for (int c0 = 0; c0 < nj; c0 += TK) {
       const int nv = min(TK, nj - c0);
-      __syncthreads();
-      for (int idx = tid; idx < nv * D; idx += 128) {
-        const int key = idx / D, d = idx - key * D;
-        const size_t src = head_off + (size_t)kmap(c0 + key) * D + d;
-        Ks[key][d] = k[src];
-        Vs[key][d] = v[src];
+      // Stage the tile in 16-byte pieces, K then V, each tensor's loads all
+      // issued before its stores; rows past nv repeat the last valid key
+      // (finite, never used).
+      constexpr int Q4 = D / 4, PER = TK * Q4 / 128;
+      uint32_t src[PER];   // element offsets within the head
+#pragma unroll
+      for (int it = 0; it < PER; ++it) {
+        const int idx = tid + it * 128, key = min(idx / Q4, nv - 1), part = idx - (idx / Q4) * Q4;
+        src[it] = (uint32_t)kmap(c0 + key) * D + part * 4;
       }
+      const float* kh = k + head_off;
+      const float* vh = v + head_off;
+      float4* ks4 = reinterpret_cast<float4*>(&Ks[0][0]);
+      float4* vs4 = reinterpret_cast<float4*>(&Vs[0][0]);
+      __syncthreads();   // the previous tile's readers are done with Ks and Vs
+      float4 pc[PER];
+#pragma unroll
+      for (int it = 0; it < PER; ++it) pc[it] = *reinterpret_cast<const float4*>(kh + src[it]);
+#pragma unroll
+      for (int it = 0; it < PER; ++it) ks4[tid + it * 128] = pc[it];
+#pragma unroll
+      for (int it = 0; it < PER; ++it) pc[it] = *reinterpret_cast<const float4*>(vh + src[it]);
+#pragma unroll
+      for (int it = 0; it < PER; ++it) vs4[tid + it * 128] = pc[it];
       __syncthreads();
-      for (int key = 0; key < nv; ++key) {
-        float s = 0.0f;
+      // SK keys at a time: their dot products are independent chains, and
+      // the running max and rescale are updated once per group.  Keys past
+      // nv read stale LDS; their scores become -inf and they are skipped in
+      // the accumulation (nv is the same for the whole workgroup).
+      for (int k0 = 0; k0 < nv; k0 += SK) {
+        float sv[SK];
 #pragma unroll
-        for (int d = 0; d < D; ++d) s += qv[d] * Ks[key][d];
-        s *= scale;
-        const float m_new = fmaxf(m_run, s);
-        const float alpha = expf(m_run - m_new);
-        const float p = expf(s - m_new);
-        l_run = l_run * alpha + p;
+        for (int x = 0; x < SK; ++x) sv[x] = 0.0f;
 #pragma unroll
-        for (int d = 0; d < D; ++d) ov[d] = ov[d] * alpha + p * Vs[key][d];
+        for (int d = 0; d < D; ++d) {
+#pragma unroll
+          for (int x = 0; x < SK; ++x) sv[x] += qv[d] * Ks[k0 + x][d];
+        }
+        float mt = -INFINITY;
+#pragma unroll
+        for (int x = 0; x < SK; ++x) {
+          sv[x] = k0 + x < nv ? sv[x] * scale : -INFINITY;
+          mt = fmaxf(mt, sv[x]);
+        }
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = expf(m_run - m_new);   // 0 on the first group (m_run = -inf)
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < D; ++d) ov[d] *= alpha;
+#pragma unroll
+        for (int x = 0; x < SK; ++x) {
+          if (k0 + x < nv) {
+            const float p = expf(sv[x] - m_new);
+            l_run += p;
+#pragma unroll
+            for (int d = 0; d < D; ++d) ov[d] += p * Vs[k0 + x][d];
+          }
+        }
         m_run = m_new;
       }
     }
