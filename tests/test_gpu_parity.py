@@ -162,6 +162,25 @@ def test_run_twice_bitwise(vsa):
     assert torch.equal(o1, o2)
 
 
+def test_side_stream_matches_current_stream(vsa):
+    """The calls enqueue on the caller's current stream: planning and
+    attention issued on a second stream (default priority), after it waits
+    for the inputs, give the same index and output bit for bit."""
+    w = W.custom("strm", 1, 3, 128, (9, 14, 20), (4, 4, 8), "bf16", 0.25, 1, "smooth")
+    _say("[gpu] side stream")
+    inp = W.generate(w, seed=15)
+    q, k, v, idx1, o1 = _run(vsa, w, inp)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        idx2 = vsa.plan(q, k, w.grid, w.block, [float(d) for d in inp["density"]], w.window_t)
+        o2 = vsa.attn(q, k, v, idx2)
+    side.synchronize()
+    assert torch.equal(idx1.row_ptr, idx2.row_ptr)
+    assert torch.equal(idx1.col_idx[: idx1.nnz()], idx2.col_idx[: idx2.nnz()])
+    assert torch.equal(o1, o2)
+
+
 # ---------------------------------------------------------------- full size
 
 FULL = ["tiny_fp32", "tiny_fp32_dense", "wan13b", "hunyuan", "wan14b_mixed", "long4x"]
