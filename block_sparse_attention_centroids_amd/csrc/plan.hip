@@ -589,9 +589,11 @@ hipError_t launch_extremes(const void* x0, float* max0, float* min0, int mid0, c
 // LDS of a workgroup with RT rows: RT rows of NB uint32 keys.
 size_t select_lds_bytes(int RT, int NB) { return (size_t)RT * NB * 4; }
 
-// Rows per workgroup: the most rows whose LDS fits in 64 KiB.
+// Rows per workgroup: up to 4 (so that a CU holds about four workgroups
+// at the headline, enough to cover the load latencies of phase 1), fewer
+// when the rows' LDS would pass 64 KiB.
 int select_rows_per_block(int NB) {
-  for (int RT = 8; RT >= 2; RT >>= 1)
+  for (int RT = 4; RT >= 2; RT >>= 1)
     if (select_lds_bytes(RT, NB) <= 65536) return RT;
   return 1;
 }
@@ -601,7 +603,6 @@ void launch_score_select_t(int RT, dim3 grid, dim3 block, size_t lds, hipStream_
                            const DGeo& g, int D, int heads, const SelectArgs& sa, int32_t* row_ptr,
                            int32_t* col_idx, int32_t* counts, uint64_t* bits) {
   switch (RT) {
-    case 8: hipLaunchKernelGGL((score_select_kernel<8, TOPP, EST>), grid, block, lds, st, sm, g, D, heads, sa, row_ptr, col_idx, counts, bits); break;
     case 4: hipLaunchKernelGGL((score_select_kernel<4, TOPP, EST>), grid, block, lds, st, sm, g, D, heads, sa, row_ptr, col_idx, counts, bits); break;
     case 2: hipLaunchKernelGGL((score_select_kernel<2, TOPP, EST>), grid, block, lds, st, sm, g, D, heads, sa, row_ptr, col_idx, counts, bits); break;
     default: hipLaunchKernelGGL((score_select_kernel<1, TOPP, EST>), grid, block, lds, st, sm, g, D, heads, sa, row_ptr, col_idx, counts, bits); break;
