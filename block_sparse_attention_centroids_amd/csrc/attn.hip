@@ -484,7 +484,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #define VSA_STEP(SC, SN, VT, KT, HAS_NEXT, NVN)                                               \
   {                                                                                           \
     const float mb = m_run * scale_log2;                                                      \
-    __builtin_amdgcn_s_setprio(1); /* matrix-heavy block: win issue ties with the other wave */ \
+    __builtin_amdgcn_s_setprio(3); /* matrix-heavy block: win issue ties with the other wave */ \
     SN = qk_tile<D>((KT), kaddr, qf);                                                         \
     const bf16x8_t p0 = probs(SC, 0, scale_log2, mb, l_run);                                  \
     const bf16x8_t p1 = probs(SC, 1, scale_log2, mb, l_run);                                  \
@@ -525,7 +525,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
       m_run = m_new;                                                                          \
     }                                                                                         \
     const float mb = m_run * scale_log2;                                                      \
-    __builtin_amdgcn_s_setprio(1);                                                            \
+    __builtin_amdgcn_s_setprio(3);                                                            \
     const bf16x8_t p0 = probs(S, 0, scale_log2, mb, l_run);                                   \
     const bf16x8_t p1 = probs(S, 1, scale_log2, mb, l_run);                                   \
     pv_step<D>((VT), vaddr, 0, p0, acc);                                                      \
