@@ -1,4 +1,5 @@
-"""Seeded random configurations through the C ABI against the CPU oracle.
+"""Seeded random configurations through the C ABI against the CPU oracle:
+selection plans (plan_select) and mixed per-head plans (plan_mixed).
 
 Each case draws a grid, a block (at most 128 tokens, often not dividing the
 grid), d, dtype, heads, batch, selection mode, estimator, window, sink
@@ -16,6 +17,7 @@ import torch
 
 import workloads as W
 from oracle import dsa_oracle as E
+from oracle import mixed_oracle as M
 from oracle import vsa_oracle as O
 from select_check import check_index
 
@@ -77,6 +79,64 @@ def test_random_configuration(vsa, seed):
     ci = idx.col_idx.cpu().numpy()[: int(rp[-1])]
     scale = 1.0 / math.sqrt(c["D"]) if c["scale"] is None else c["scale"]
     check_index(rp, ci, S, g, c["mode"], c["vals"], c["window"], c["sink"], scale)
+    ref = O.attention(inp["q"], inp["k"], inp["v"], c["grid"], c["block"], rp, ci)
+    err = np.abs(o.float().cpu().numpy().astype(np.float64) - ref)
+    if c["dtype"] == "bf16":
+        assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN, (err.max(), err.mean())
+    else:
+        assert err.max() <= F32_MAX, err.max()
+
+
+N_MIXED = 16
+
+
+def _mixed_case(seed):
+    rng = np.random.default_rng(seed)
+    while True:
+        block = tuple(int(x) for x in rng.integers(1, 9, size=3))
+        if math.prod(block) <= 128:
+            break
+    while True:
+        grid = tuple(int(x) for x in (rng.integers(1, 9), rng.integers(1, 25), rng.integers(1, 33)))
+        if math.prod(grid) <= 2000:
+            break
+    heads = int(rng.integers(1, 5))
+    options = []
+    for _ in range(heads):
+        kind = str(rng.choice(["dynamic", "static", "dense"]))
+        o = {"kind": kind}
+        if kind != "dense":
+            o["value"] = float(np.float32(rng.uniform(0.02, 1.0)))
+        wt = int(rng.choice([-1, -1, 0, 1]))
+        if wt >= 0:
+            o["window_t"] = wt
+        options.append(o)
+    return dict(grid=grid, block=block, D=int(rng.choice([64, 128])), dtype=str(rng.choice(["bf16", "f32"])),
+                heads=heads, B=int(rng.integers(1, 3)), est=str(rng.choice(["mean", "dsa", "dsa2"])),
+                options=options, gen=str(rng.choice(["smooth", "iid"])), table_seed=int(rng.integers(1 << 30)))
+
+
+@pytest.mark.parametrize("seed", range(N_MIXED))
+def test_random_mixed_plan(vsa, seed):
+    c = _mixed_case(8000 + seed)
+    print(f"[gpu] random mixed case {seed}: {c}", flush=True)
+    sys.stdout.flush()
+    w = W.custom(f"rm{seed}", c["B"], c["heads"], c["D"], c["grid"], c["block"], c["dtype"], 0.5, -1, c["gen"])
+    g = O.geometry(c["grid"], c["block"])
+    inp = W.generate(w, seed=9500 + seed)
+    trng = np.random.default_rng(c["table_seed"])
+    table = (np.round(trng.standard_normal((c["heads"], g.NB, g.NB)) * 8) / 8).astype(np.float32)   # ties
+    dt = torch.bfloat16 if c["dtype"] == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(inp[n])).to(device="cuda", dtype=dt).contiguous()
+               for n in ("q", "k", "v"))
+    idx = vsa.plan_mixed(q, k, c["grid"], c["block"], c["options"], torch.from_numpy(table).cuda(), c["est"])
+    o = vsa.attn(q, k, v, idx)
+    torch.cuda.synchronize()
+    rp, ci, _ = M.plan_mixed(inp["q"], inp["k"], c["grid"], c["block"], c["options"], table, c["est"])
+    grp = idx.row_ptr.cpu().numpy()
+    gci = idx.col_idx.cpu().numpy()[: int(grp[-1])]
+    assert np.array_equal(grp, rp), "row_ptr differs"
+    assert np.array_equal(gci, ci), "col_idx differs"
     ref = O.attention(inp["q"], inp["k"], inp["v"], c["grid"], c["block"], rp, ci)
     err = np.abs(o.float().cpu().numpy().astype(np.float64) - ref)
     if c["dtype"] == "bf16":
