@@ -1,5 +1,6 @@
 """Seeded random configurations through the C ABI against the CPU oracle:
-selection plans (plan_select) and mixed per-head plans (plan_mixed).
+selection plans (plan_select), mixed per-head plans (plan_mixed) and
+head-wise blocking-scheme selection (select_scheme).
 
 Each case draws a grid, a block (at most 128 tokens, often not dividing the
 grid), d, dtype, heads, batch, selection mode, estimator, window, sink
@@ -18,6 +19,7 @@ import torch
 import workloads as W
 from oracle import dsa_oracle as E
 from oracle import mixed_oracle as M
+from oracle import sics_oracle as SC
 from oracle import vsa_oracle as O
 from select_check import check_index
 
@@ -143,3 +145,40 @@ def test_random_mixed_plan(vsa, seed):
         assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN, (err.max(), err.mean())
     else:
         assert err.max() <= F32_MAX, err.max()
+
+
+N_SCHEME = 8
+SCHEME_RTOL, SCHEME_ATOL = 1e-4, 1e-3   # the scheme tests' bar: float32 sums of unit vectors
+
+
+@pytest.mark.parametrize("seed", range(N_SCHEME))
+def test_random_scheme_selection(vsa, seed):
+    rng = np.random.default_rng(8500 + seed)
+    while True:
+        grid = tuple(int(x) for x in (rng.integers(1, 9), rng.integers(1, 25), rng.integers(1, 33)))
+        if math.prod(grid) <= 2000:
+            break
+    cands = []
+    while len(cands) < int(rng.integers(1, 6)):
+        b = tuple(int(x) for x in rng.integers(1, 9, size=3))
+        if math.prod(b) <= 128 and b not in cands:
+            cands.append(b)
+    D, dtype = int(rng.choice([64, 128])), str(rng.choice(["bf16", "f32"]))
+    heads, B = int(rng.integers(1, 4)), int(rng.integers(1, 3))
+    print(f"[gpu] random scheme case {seed}: grid={grid} D={D} {dtype} heads={heads} B={B} cands={cands}",
+          flush=True)
+    sys.stdout.flush()
+    w = W.custom(f"rs{seed}", B, heads, D, grid, cands[0], dtype, 0.5, -1, str(rng.choice(["smooth", "iid"])))
+    inp = W.generate(w, seed=9700 + seed)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q, k = (torch.from_numpy(np.ascontiguousarray(inp[n])).to(device="cuda", dtype=dt).contiguous()
+            for n in ("q", "k"))
+    scores, choice = vsa.select_scheme(q, k, grid, cands)
+    torch.cuda.synchronize()
+    ref = SC.scheme_scores(inp["q"], inp["k"], grid, cands).reshape(len(cands), B * heads)
+    got = scores.cpu().numpy()
+    np.testing.assert_allclose(got, ref, rtol=SCHEME_RTOL, atol=SCHEME_ATOL)
+    best = ref.max(axis=0)
+    for bh, c in enumerate(choice.cpu().numpy().tolist()):
+        assert 0 <= c < len(cands)
+        assert ref[c, bh] >= best[bh] - SCHEME_RTOL * abs(best[bh]) - SCHEME_ATOL, (bh, c, ref[:, bh])
