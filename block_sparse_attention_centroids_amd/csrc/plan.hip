@@ -511,6 +511,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
 }
 
 // Bitmap rows -> ascending column lists at row_ptr (one wave per row).
+// Every write stays in [0, capacity), whatever row_ptr holds.
 __global__ __launch_bounds__(256) void fill_kernel(const uint64_t* __restrict__ bits,
                                                    const int32_t* __restrict__ row_ptr,
                                                    int32_t* __restrict__ col_idx, int64_t R, int words,
@@ -524,7 +525,7 @@ __global__ __launch_bounds__(256) void fill_kernel(const uint64_t* __restrict__ 
     const uint64_t w = bits[row * words + s];
     const int j = s * 64 + lane;
     const int64_t pos = base + __popcll(w & lt);
-    if (j < NB && ((w >> lane) & 1ull) && pos < capacity) col_idx[pos] = j;
+    if (j < NB && ((w >> lane) & 1ull) && pos >= 0 && pos < capacity) col_idx[pos] = j;
     base += __popcll(w);
   }
 }
