@@ -250,7 +250,11 @@ vsa_status vsa_estimate(const void* q, const void* k, const vsa_shape* shape, in
  * matrix cores with float32 accumulation and a float32 online softmax; f32
  * computes in float32.  A row of the index with no key blocks (never
  * produced by the planners) gives zeros for its query tokens.  ws may be
- * NULL when attn_ws is 0. */
+ * NULL when attn_ws is 0.
+ * The index arrays are device data, read as given (the host checks only
+ * the shape): row_ptr must be non-decreasing from 0 with its last entry at
+ * most capacity, and every col_idx entry in use must lie in [0, nb), as the
+ * planners write them.  An index that breaks this is undefined behaviour. */
 vsa_status vsa_attn(const void* q, const void* k, const void* v, const vsa_index* index,
                     float scale, void* o, void* ws, size_t ws_bytes, void* stream);
 
