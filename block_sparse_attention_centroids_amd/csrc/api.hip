@@ -34,11 +34,6 @@ DGeo to_dgeo(const Geo& g) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool same_shape(const vsa_shape& a, const vsa_shape& b) {
-  return a.B == b.B && a.heads == b.heads && a.D == b.D && a.T == b.T && a.H == b.H &&
-         a.W == b.W && a.bt == b.bt && a.bh == b.bh && a.bw == b.bw && a.dtype == b.dtype;
-}
-
 vsa_status hip_status(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_HIP; }
 
 // Enqueue the block summaries of the estimator into the workspace regions

@@ -47,7 +47,6 @@ typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int KS = 64;              // keys per stage
-constexpr int KT = KS / 32;         // 32-key S^T tiles per stage
 constexpr int WAVES = 4;            // waves per workgroup: 128 query tokens in all
 constexpr int THREADS = 64 * WAVES;
 constexpr float LAZY_LOG2 = 8.0f;   // running max is only raised when a row max exceeds it by 2^8
@@ -75,34 +74,24 @@ struct AttnCfg {
 
 __device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Raw buffer descriptor as four scalar dwords (base, num_records, flags):
-// loads past num_records return zero instead of faulting.
-struct Rsrc4 {
-  u32x4_t d;
-};
-__device__ inline Rsrc4 make_rsrc4(const void* base, uint32_t bytes) {
+// Buffer resource over `bytes` bytes from `base` (stride 0, raw offsets):
+// loads at or past `bytes` return zeros instead of faulting.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc4(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
-  Rsrc4 r;
-  r.d[0] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r.d[1] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));   // stride 0
-  r.d[2] = bytes;
-  r.d[3] = 0x00020000u;
-  return r;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0,
+                                           (int)bytes, 0x00020000);
 }
 
 // 16 bytes per lane from a raw buffer straight into LDS at lds_base + 16*lane
-// (out-of-range offsets write zeros).  Written as asm so that the
-// compiler's LDS-DMA tracking does not force a wait for every in-flight
-// stage before each LDS read: completion is awaited explicitly (vmcnt)
-// before the barrier that publishes a stage.  The instruction has no
-// register results.
-__device__ __forceinline__ void dma16(const Rsrc4& r, uint32_t lds_base, uint32_t voff) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
-      :
-      : "s"(lds_base), "v"(voff), "s"(r.d)
-      : "memory", "m0");
+// (out-of-range offsets write zeros), through the compiler's LDS-DMA
+// builtin: the compiler sets M0 itself and folds constant LDS offsets into
+// the instruction.  It adds no waits of its own here; completion is awaited
+// explicitly (vmcnt) before the barrier that publishes a stage.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(uintptr_t)lds_base, 16,
+                                           (int)voff, 0, 0, 0);
 }
 
 __device__ inline uint32_t lds_addr(const void* p) {
@@ -259,8 +248,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
   qmap.init(g, bi);
   const size_t head_off = (size_t)bh * g.N * D;
   const uint32_t head_bytes = (uint32_t)g.N * D * 2u;
-  const Rsrc4 krs = make_rsrc4(k + head_off, head_bytes);
-  const Rsrc4 vrs = make_rsrc4(v + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc4(k + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc4(v + head_off, head_bytes);
   const uint32_t lds0 = (uint32_t)uniform((int)lds_addr(lds));
 
   // This wave's queries: tokens [32*qt, +32) of the block.  A block of at

@@ -114,7 +114,8 @@ __device__ inline void est_column(const float* const (&qa)[RG], const float* con
                                   float (&acc)[RG]) {
 #pragma unroll
   for (int x = 0; x < RG; ++x) acc[x] = 0.0f;
-#pragma unroll (EST == 2 ? 2 : 4)   // DSA2's second query summary doubles the scalar loads
+  constexpr int UNROLL = EST == 2 ? 2 : 4;   // DSA2's second query summary doubles the scalar loads
+#pragma unroll UNROLL
   for (int d = 0; d < D; d += 4) {
     float kA[4], kB[4];
 #pragma unroll
