@@ -7,11 +7,12 @@ calls it and shares no code with it (NumPy only, plus the geometry, Top-K
 and estimators of the same oracle package).
 
 Sources:
-* DecoupAttn Plans (dataset README), introduction: a compiled plan gives
-  every unit u = (timestep, layer, head) one option -- Dense, Static_theta
-  with theta in {0.05, 0.10, 0.15, 0.20, 0.30, 0.45}, or CompOnly -- chosen
-  from an offline block ranking D_u, and every call one estimator (Full or
-  Centroid) at density 0.20.
+* DecoupAttn Plans (dataset README), introduction: the plan compiled
+  offline for a model assigns each (timestep, layer, head) unit a dense
+  option, a static top-theta option over an offline ranking of key blocks
+  (theta from a fixed menu of six keep rates, 0.05 to 0.45) or a
+  computation-only option, and assigns each call an estimator (the full
+  attention map or block centroids) that selects 20% of the blocks.
 * SPADE (arXiv 2608.03335) 3.1: each head's sparsity scheme has a
   local-window length and a Top-K keep; 3.3: the selection is united with
   the local window.

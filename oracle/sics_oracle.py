@@ -6,23 +6,26 @@ library never calls it and shares no code with it (NumPy only, plus the
 geometry of the same oracle package).
 
 Source: "SPADE: An Input-Adaptive Sparse Attention Engine for Fast Video
-Diffusion Models Inference" (arXiv 2608.03335), 3.2 Schemes Generation:
-Eq. 3 (aggregation score of a blocking scheme = sum over its blocks of
-SICS), Eq. 4 (SICS = sum of all pairwise cosine similarities inside a
-block), Eq. 5 and Algorithm 1 (the online form: normalize each token, add
-its inner product with the running sum of the previous normalized tokens to
-sigma, add it to the running sum; SICS = 2*sigma + BS).  The head's selected
-blocking scheme is the candidate with the highest aggregation score.
+Diffusion Models Inference" (arXiv 2608.03335), 3.2 Schemes Generation.
+Eq. 4 defines SICS of a block as the sum of every entry of the cosine
+similarity matrix of its tokens: with D the diagonal matrix of the token
+norms, the sum of all entries of D^-1 X X^T D^-1.  Eq. 3 sums SICS over the
+blocks of a scheme (the aggregation score AS), and the head keeps the
+candidate scheme with the highest score.  This oracle evaluates Eq. 4 as
+written, through the Gram matrix of the normalized tokens; the online
+rewrite of Eq. 5 is what the GPU evaluates, and the tests pin this module
+against the closed form ||sum of normalized tokens||^2 and SciPy's pairwise
+cosine distances independently.
 
 Readings where the pages are silent (also listed in the design notes):
 
 * R17 ragged edges: a cut-short block's SICS runs over its valid tokens
   (BS = that block's token count).
 * R18 a zero token vector normalizes to the zero vector: its cosine
-  similarity with anything, itself included, is 0, so the diagonal term BS
-  of Algorithm 1 counts the nonzero tokens only.
-* R19 a head's scheme score is AS(Q | scheme) + AS(K | scheme) (the module
-  aggregates "Q and K under each" candidate).
+  similarity with anything, itself included, is 0, so the diagonal of the
+  Gram matrix counts the nonzero tokens only.
+* R19 a head's scheme score is AS(Q | scheme) + AS(K | scheme): the module
+  scores a candidate by aggregating both Q and K under it.
 * R20 the selected scheme is the first candidate (lowest index) with the
   highest score.  The GPU decides in float32; where two candidates' float64
   scores lie within the float32 error bound of each other, either choice
@@ -37,49 +40,31 @@ import numpy as np
 from . import vsa_oracle as O
 
 
-def sics_online(xb: np.ndarray) -> float:
-    """Algorithm 1 (SPADE 3.2) in float64 for one block's tokens xb [n, d],
-    in token order: r holds the running sum of the normalized tokens seen so
-    far, sigma the sum of their inner products with each new token."""
-    xb = np.asarray(xb, dtype=np.float64)
-    r = np.zeros(xb.shape[1], dtype=np.float64)
-    sigma = 0.0
-    nonzero = 0
-    for x in xb:
-        norm = float(np.sqrt(np.dot(x, x)))
-        if norm == 0.0:      # R18
-            continue
-        xh = x / norm
-        sigma += float(np.dot(r, xh))
-        r += xh
-        nonzero += 1
-    return 2.0 * sigma + nonzero
+def _normalized(x: np.ndarray) -> np.ndarray:
+    """Rows of x (last axis = channels) divided by their Euclidean norm, in
+    float64; a zero row stays zero (R18)."""
+    x = np.asarray(x, dtype=np.float64)
+    norm = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return np.divide(x, norm, out=np.zeros_like(x), where=norm > 0.0)
 
 
-def _sics_online_many(xb: np.ndarray) -> np.ndarray:
-    """Algorithm 1 run side by side on many blocks of the same token count:
-    xb [m, n, d] -> [m], each block with exactly the steps of sics_online."""
-    xb = np.asarray(xb, dtype=np.float64)
-    m, n, d = xb.shape
-    r = np.zeros((m, d), dtype=np.float64)
-    sigma = np.zeros(m, dtype=np.float64)
-    nonzero = np.zeros(m, dtype=np.float64)
-    for t in range(n):
-        x = xb[:, t, :]
-        norm = np.sqrt(np.einsum("md,md->m", x, x))
-        ok = norm > 0.0
-        xh = np.where(ok[:, None], x / np.where(ok, norm, 1.0)[:, None], 0.0)
-        sigma += np.where(ok, np.einsum("md,md->m", r, xh), 0.0)
-        r += xh
-        nonzero += ok
-    return 2.0 * sigma + nonzero
+def sics(xb: np.ndarray) -> float:
+    """Eq. 4 for one block's tokens xb [n, d]: the sum of all entries of the
+    n x n cosine similarity matrix (normalized Gram matrix), float64."""
+    xh = _normalized(xb)
+    return float((xh @ xh.T).sum())
+
+
+def _sics_many(xb: np.ndarray) -> np.ndarray:
+    """Eq. 4 for many blocks of the same token count: xb [m, n, d] -> [m]."""
+    xh = _normalized(xb)
+    return np.matmul(xh, np.swapaxes(xh, 1, 2)).sum(axis=(1, 2))
 
 
 def block_sics(x: np.ndarray, g: "O.Geometry", heads: Sequence[int] = None) -> np.ndarray:
     """SICS of every block of x [B, heads, N, d] under the blocking of g:
-    float64 [B, heads, NB], each block by Algorithm 1 over its tokens in
-    block order (R17).  heads limits the work to some heads (the others
-    stay zero)."""
+    float64 [B, heads, NB], each block by Eq. 4 over its valid tokens (R17).
+    heads limits the work to some heads (the others stay zero)."""
     B, Hh = x.shape[:2]
     out = np.zeros((B, Hh, g.NB), dtype=np.float64)
     hs = range(Hh) if heads is None else heads
@@ -88,7 +73,7 @@ def block_sics(x: np.ndarray, g: "O.Geometry", heads: Sequence[int] = None) -> n
         idx = np.stack([g.tokens[j] for j in js])          # [m, size]
         for b in range(B):
             for h in hs:
-                out[b, h, js] = _sics_online_many(x[b, h][idx])
+                out[b, h, js] = _sics_many(x[b, h][idx])
     return out
 
 

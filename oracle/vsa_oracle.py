@@ -282,18 +282,6 @@ def attention(q, k, v, grid, block, row_ptr, col_idx, scale: Optional[float] = N
     return out
 
 
-def dense_attention(q, k, v, scale: Optional[float] = None) -> np.ndarray:
-    """Eq. 1 of SPADE 2.2 in float64, [B, Hh, N, D]."""
-    D = q.shape[-1]
-    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    q64, k64, v64 = (a.astype(np.float64) for a in (q, k, v))
-    out = np.empty(q64.shape[:-1] + (v64.shape[-1],))
-    for b in range(q.shape[0]):
-        for h in range(q.shape[1]):
-            out[b, h] = _softmax_rows((q64[b, h] @ k64[b, h].T) * sc) @ v64[b, h]
-    return out
-
-
 # --------------------------------------------------------------------------
 # accounting (SPADE 4.1 Metrics: sparsity is the fraction of pruned scores)
 # --------------------------------------------------------------------------

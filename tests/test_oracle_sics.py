@@ -1,6 +1,5 @@
-"""Pins for the SICS / aggregation-score oracle (SPADE 3.2, Eq. 3-5 and
-Algorithm 1): each checks the oracle against something other than its own
-formula -- the closed form ||sum of normalized tokens||^2, SciPy's cosine
+"""Pins for the SICS / aggregation-score oracle (SPADE 3.2, Eq. 3 and 4):
+each checks the oracle against something other than its own formula -- the closed form ||sum of normalized tokens||^2, SciPy's cosine
 distance, special cases with known values, a hand-worked example and a
 constructed input whose best blocking scheme is known."""
 import json
@@ -26,34 +25,34 @@ def _closed_form(xb):
 
 
 @pytest.mark.parametrize("n,d,seed", [(1, 4, 0), (7, 3, 1), (64, 128, 2), (128, 64, 3), (33, 128, 4)])
-def test_online_equals_closed_form(n, d, seed):
+def test_sics_equals_closed_form(n, d, seed):
     xb = np.random.default_rng(seed).standard_normal((n, d))
-    assert S.sics_online(xb) == pytest.approx(_closed_form(xb), rel=1e-12, abs=1e-9)
+    assert S.sics(xb) == pytest.approx(_closed_form(xb), rel=1e-12, abs=1e-9)
 
 
 @pytest.mark.parametrize("n,d,seed", [(5, 3, 0), (40, 16, 1), (128, 128, 2)])
-def test_online_equals_scipy_pairwise_cosine(n, d, seed):
+def test_sics_equals_scipy_pairwise_cosine(n, d, seed):
     xb = np.random.default_rng(seed).standard_normal((n, d)) + 0.3
     pairwise = 1.0 - cdist(xb, xb, metric="cosine")   # Eq. 4 via a library routine
-    assert S.sics_online(xb) == pytest.approx(pairwise.sum(), rel=1e-10, abs=1e-8)
+    assert S.sics(xb) == pytest.approx(pairwise.sum(), rel=1e-10, abs=1e-8)
 
 
 def test_special_cases():
     rng = np.random.default_rng(5)
     v = rng.standard_normal(32)
     # identical tokens: every cosine is 1 -> BS^2
-    assert S.sics_online(np.tile(v, (10, 1))) == pytest.approx(100.0, rel=1e-12)
+    assert S.sics(np.tile(v, (10, 1))) == pytest.approx(100.0, rel=1e-12)
     # orthonormal tokens: only the diagonal -> BS
     q, _ = np.linalg.qr(rng.standard_normal((32, 12)))
-    assert S.sics_online(q.T * rng.uniform(0.5, 3.0, (12, 1))) == pytest.approx(12.0, abs=1e-9)
+    assert S.sics(q.T * rng.uniform(0.5, 3.0, (12, 1))) == pytest.approx(12.0, abs=1e-9)
     # antipodal pairs: the normalized sum vanishes -> 0
     w = rng.standard_normal((6, 32))
-    assert S.sics_online(np.concatenate([w, -2.0 * w])) == pytest.approx(0.0, abs=1e-9)
+    assert S.sics(np.concatenate([w, -2.0 * w])) == pytest.approx(0.0, abs=1e-9)
     # positive scaling of tokens and their order do not matter
     x = rng.standard_normal((20, 8))
-    base = S.sics_online(x)
-    assert S.sics_online(x * rng.uniform(0.1, 10.0, (20, 1))) == pytest.approx(base, rel=1e-12)
-    assert S.sics_online(x[rng.permutation(20)]) == pytest.approx(base, rel=1e-12)
+    base = S.sics(x)
+    assert S.sics(x * rng.uniform(0.1, 10.0, (20, 1))) == pytest.approx(base, rel=1e-12)
+    assert S.sics(x[rng.permutation(20)]) == pytest.approx(base, rel=1e-12)
     # bounds: 0 <= SICS <= BS^2
     assert 0.0 <= base <= 400.0
 
@@ -63,13 +62,13 @@ def test_zero_token_reading():
     rng = np.random.default_rng(6)
     x = rng.standard_normal((9, 5))
     with_zero = np.concatenate([x[:4], np.zeros((1, 5)), x[4:]])
-    assert S.sics_online(with_zero) == pytest.approx(S.sics_online(x), rel=1e-12)
-    assert S.sics_online(np.zeros((3, 5))) == 0.0
+    assert S.sics(with_zero) == pytest.approx(S.sics(x), rel=1e-12)
+    assert S.sics(np.zeros((3, 5))) == 0.0
 
 
 def test_hand_example():
     ex = json.load(open(os.path.join(HERE, "golden", "sics_hand_example.json")))
-    assert S.sics_online(np.array(ex["block"])) == pytest.approx(ex["sics_value"], rel=1e-14)
+    assert S.sics(np.array(ex["block"])) == pytest.approx(ex["sics_value"], rel=1e-14)
     assert ex["sics_value"] == pytest.approx(3.0 + 2.0 * math.sqrt(2.0), rel=1e-14)
 
 
@@ -126,4 +125,4 @@ def test_vectorized_blocks_match_one_block_at_a_time():
     bs = S.block_sics(x, g)
     for h in range(2):
         for j in range(g.NB):
-            assert bs[0, h, j] == pytest.approx(S.sics_online(x[0, h, g.tokens[j]]), rel=1e-12, abs=1e-12)
+            assert bs[0, h, j] == pytest.approx(S.sics(x[0, h, g.tokens[j]]), rel=1e-12, abs=1e-12)
