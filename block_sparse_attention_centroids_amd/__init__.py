@@ -232,6 +232,17 @@ def plan_mixed(q: Optional[torch.Tensor], k: Optional[torch.Tensor], grid, block
     return Index(cidx.shape, cidx.nb, cidx.window_t, row_ptr, col_idx, cap, cidx.equal_heads)
 
 
+def _check_out(q: torch.Tensor, out: torch.Tensor) -> None:
+    """The kernels write every valid token row of `out` in raster order, so
+    it must be exactly q's shape, dtype and device, and contiguous."""
+    if not isinstance(out, torch.Tensor):
+        raise TypeError("out must be a tensor")
+    if out.shape != q.shape or out.dtype != q.dtype or out.device != q.device:
+        raise ValueError(f"out must match q: shape {tuple(q.shape)}, dtype {q.dtype}, device {q.device}")
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+
+
 def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: Index,
          scale: Optional[float] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Block-sparse attention over the kept blocks; output in raster order."""
@@ -243,6 +254,8 @@ def attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: Index,
     if (shape.B, shape.heads, shape.D, shape.dtype) != (index.shape.B, index.shape.heads,
                                                          index.shape.D, index.shape.dtype):
         raise ValueError("index was planned for another shape")
+    if out is not None:
+        _check_out(q, out)
     o = torch.empty_like(q) if out is None else out
     cidx = index.c_index()
     check(lib.vsa_attn(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),

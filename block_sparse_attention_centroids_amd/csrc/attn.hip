@@ -298,9 +298,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // may take its tiles from two blocks (of at most 32 tokens each).  The
   // block ids of the next two entries are fetched ahead into jn1/jn2 by
   // scalar loads (the ids are wave-uniform).  A scalar load is waited on
-  // through lgkmcnt, which the K/V loads to LDS do not touch: a vector load
-  // here would make the compiler's wait for the id (vmcnt, which does not
-  // see the inline-asm K/V loads) also wait for the stage just issued.
+  // through lgkmcnt, which the K/V loads to LDS do not touch: the id of a
+  // vector load would be waited on through vmcnt, and that wait would also
+  // cover the K/V direct-to-LDS loads of the stage just issued.
   // Entries are read only below e_end, inside the row.
   const int row = bh * g.NB + i;
   const int e_end = uniform(row_ptr[row + 1]);

@@ -62,6 +62,13 @@ inline int window_count(const Geo& g, int tb, int window_t) {
   return (hi - lo + 1) * g.nbh * g.nbw;
 }
 
+// A window radius of nbt - 1 already covers every temporal block, so a
+// larger one selects the same key blocks; clamping keeps the radius in the
+// 16-bit field the selection kernel reads, whatever the caller passed.
+inline int clamp_window(const Geo& g, int window_t) {
+  return window_t < 0 ? -1 : std::min(window_t, g.nbt - 1);
+}
+
 inline int elt_bytes(int dtype) { return dtype == VSA_F32 ? 4 : 2; }
 
 // Shape validation shared by every entry point.
@@ -144,6 +151,7 @@ inline vsa_status select_sizes(const vsa_shape* s, const vsa_select* sel, PlanSi
   if (s->heads > VSA_MAX_HEADS) return VSA_ERR_UNSUPPORTED;
   Geo g = make_geo(*s);
   if (sel->sink < 0 || sel->sink > g.NB) return VSA_ERR_INVALID_ARG;
+  const int window_t = clamp_window(g, sel->window_t);
   if (!(sel->scale >= 0.0f) || !std::isfinite(sel->scale)) return VSA_ERR_INVALID_ARG;
   const bool topp = sel->mode == VSA_TOPP;
   out->k.assign(s->heads, 0);
@@ -166,7 +174,7 @@ inline vsa_status select_sizes(const vsa_shape* s, const vsa_select* sel, PlanSi
       int64_t per_head = 0;
       for (int i = 0; i < g.NB; ++i) {
         int tb = i / (g.nbh * g.nbw);
-        int64_t c = int64_t(out->k[h]) + window_count(g, tb, sel->window_t) + sel->sink;
+        int64_t c = int64_t(out->k[h]) + window_count(g, tb, window_t) + sel->sink;
         per_head += std::min<int64_t>(c, g.NB);
       }
       cap += per_head;
@@ -176,13 +184,13 @@ inline vsa_status select_sizes(const vsa_shape* s, const vsa_select* sel, PlanSi
   if (cap >= (int64_t(1) << 31) - 1) return VSA_ERR_UNSUPPORTED;
   out->capacity = cap;
   out->estimator = sel->estimator;
-  out->win.assign(s->heads, sel->window_t);
+  out->win.assign(s->heads, window_t);
   out->kind.assign(s->heads, VSA_HEAD_DYNAMIC);
   out->any_dynamic = true;
   out->any_static = false;
-  out->max_win = sel->window_t;
+  out->max_win = window_t;
   out->words = (g.NB + 63) / 64;
-  out->bitmap = topp || sel->window_t >= 0 || sel->sink > 0;
+  out->bitmap = topp || window_t >= 0 || sel->sink > 0;
   layout_workspace(s, out);
   return VSA_OK;
 }
@@ -209,7 +217,7 @@ inline vsa_status mixed_sizes(const vsa_shape* s, const vsa_head_option* opts, i
     const vsa_head_option& o = opts[h];
     if (o.kind != VSA_HEAD_DYNAMIC && o.kind != VSA_HEAD_STATIC && o.kind != VSA_HEAD_DENSE)
       return VSA_ERR_INVALID_ARG;
-    if (o.window_t < -1 || o.window_t > 32767) return VSA_ERR_INVALID_ARG;
+    if (o.window_t < -1) return VSA_ERR_INVALID_ARG;
     if (o.kind == VSA_HEAD_DENSE) {
       out->k[h] = g.NB;
     } else {
@@ -217,10 +225,10 @@ inline vsa_status mixed_sizes(const vsa_shape* s, const vsa_head_option* opts, i
       out->k[h] = k_rule(o.value, g.NB);
     }
     out->kind[h] = o.kind;
-    out->win[h] = o.window_t;
+    out->win[h] = clamp_window(g, o.window_t);
     out->any_dynamic = out->any_dynamic || o.kind == VSA_HEAD_DYNAMIC;
     out->any_static = out->any_static || o.kind == VSA_HEAD_STATIC;
-    out->max_win = std::max(out->max_win, o.window_t);
+    out->max_win = std::max(out->max_win, out->win[h]);
   }
   out->estimator = estimator;
   out->scale = 1.0f;

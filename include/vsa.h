@@ -106,7 +106,10 @@ typedef struct {
  * density: host float[n_density], n_density = 1 (all heads) or heads; each
  *   value in (0, 1].  k_h = min(NB, max(1, floor(density_h*NB + 0.5))).
  * window_t: -1 for none, r >= 0 to also keep every key block whose temporal
- *   block index is within +-r of the query block's.
+ *   block index is within +-r of the query block's.  Any r >= nbt - 1
+ *   covers every temporal block; such a radius is treated as nbt - 1 (the
+ *   same key blocks), and a plan records nbt - 1 in index->window_t.
+ *   Values below -1 are VSA_ERR_INVALID_ARG.
  * Outputs (any may be NULL): row_ptr_len = B*heads*NB + 1; col_capacity =
  *   an upper bound of the kept entries (exact without a window);
  *   plan_ws / attn_ws = workspace bytes that vsa_plan / vsa_attn need. */
@@ -206,8 +209,8 @@ typedef enum { VSA_HEAD_DYNAMIC = 0, VSA_HEAD_STATIC = 1, VSA_HEAD_DENSE = 2 } v
  *   scores of this call's Q and K) and VSA_HEAD_STATIC (over the caller's
  *   static score table); k as in vsa_query.  Ignored for VSA_HEAD_DENSE,
  *   which keeps every key block.
- * window_t: -1 or 0 <= r <= 32767, this head's temporal window as in
- *   vsa_query. */
+ * window_t: -1 or r >= 0, this head's temporal window as in vsa_query
+ *   (a radius above nbt - 1 is treated as nbt - 1). */
 typedef struct {
   int32_t kind;
   float value;

@@ -78,6 +78,38 @@ def test_query_matches_oracle_geometry(lib, name):
     assert aws == 0
 
 
+@pytest.mark.parametrize("window_t", [5, 6, 32767, 32768, 70000, 2**31 - 1])
+def test_large_window_is_the_full_window(lib, window_t):
+    """A window radius at or beyond nbt - 1 keeps every temporal block, so
+    each sizing entry point must answer exactly as for nbt - 1 (Wan grid:
+    nbt = 6) instead of letting the radius reach the selection kernel in a
+    narrowed form."""
+    w = W.WORKLOADS["wan13b"]
+    g = O.geometry(w.grid, w.block)
+    assert g.nbt == 6
+    full = _query(lib, _shape(w), [0.2], g.nbt - 1)
+    got = _query(lib, _shape(w), [0.2], window_t)
+    assert got[0] == 0 and got[1:] == full[1:]
+    assert full[2] == w.B * w.heads * g.NB * g.NB      # every row holds every block
+    sel, _keep = _select(_lib.VSA_TOPK, [0.2], window_t=window_t)
+    sel_full, _keep2 = _select(_lib.VSA_TOPK, [0.2], window_t=g.nbt - 1)
+    a, b = [], []
+    for s_, out in ((sel, a), (sel_full, b)):
+        rl, cap, pws = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
+        assert lib.vsa_query_select(ctypes.byref(_shape(w)), ctypes.byref(s_), ctypes.byref(rl),
+                                    ctypes.byref(cap), ctypes.byref(pws)) == 0
+        out += [rl.value, cap.value, pws.value]
+    assert a == b
+    shape = _shape(w)
+    caps = []
+    for r in (window_t, g.nbt - 1):
+        cap = ctypes.c_int64()
+        assert lib.vsa_query_mixed(ctypes.byref(shape), _opts(*[(0, 0.2, r)] * w.heads), 0, None,
+                                   ctypes.byref(cap), None) == 0
+        caps.append(cap.value)
+    assert caps[0] == caps[1]
+
+
 def test_query_rejects_bad_arguments(lib):
     w = W.WORKLOADS["wan13b"]
     ok = _shape(w)
@@ -343,7 +375,7 @@ def test_mixed_entry_error_paths():
     assert q([(0, 0.0, -1)] + ok[1:]) == _lib.VSA_ERR_INVALID_ARG
     assert q([(1, 1.5, -1)] + ok[1:]) == _lib.VSA_ERR_INVALID_ARG
     assert q([(2, 0.0, -2)] + ok[1:]) == _lib.VSA_ERR_INVALID_ARG
-    assert q([(2, 0.0, 40000)] + ok[1:]) == _lib.VSA_ERR_INVALID_ARG
+    assert q([(2, 0.0, 40000)] + ok[1:]) == 0                  # past nbt - 1: the full window
     assert q([(2, 0.0, 3)] + ok[1:]) == 0                      # dense ignores value
     assert lib.vsa_query_mixed(ctypes.byref(shape), None, 0, None, None, None) == _lib.VSA_ERR_INVALID_ARG
     rl, cap, pws = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
@@ -395,3 +427,24 @@ def test_balanced_xcd_mapping_is_a_bijection(NB, BH):
             rows = [i for hh, i in per_xcd[x] if hh == h]
             assert rows == list(range(rows[0], rows[0] + len(rows)))   # contiguous slice
             assert len(rows) in (NB // 8, NB // 8 + 1)
+
+
+def test_attn_out_argument_is_checked_before_any_launch():
+    """attn(out=...) hands `out` to the kernels, which write every valid
+    token row in raster order: a wrong shape, dtype or layout must raise
+    before anything is launched (checked here on host tensors)."""
+    import torch
+
+    from block_sparse_attention_centroids_amd import _check_out
+    q = torch.zeros((1, 2, 256, 64), dtype=torch.bfloat16)
+    _check_out(q, torch.empty_like(q))
+    with pytest.raises(ValueError):
+        _check_out(q, torch.empty((1, 2, 255, 64), dtype=torch.bfloat16))      # short
+    with pytest.raises(ValueError):
+        _check_out(q, torch.empty((1, 2, 256, 64), dtype=torch.float32))       # dtype
+    with pytest.raises(ValueError):
+        _check_out(q, torch.empty((1, 2, 64, 256), dtype=torch.bfloat16).transpose(2, 3))   # strided
+    with pytest.raises(ValueError):
+        _check_out(q, torch.empty((2, 1, 256, 64), dtype=torch.bfloat16))      # same numel, other shape
+    with pytest.raises(TypeError):
+        _check_out(q, None)

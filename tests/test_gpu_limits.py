@@ -96,3 +96,23 @@ def test_max_blocks_sampled_rows(vsa, mode, value):
             c = len(got)
             assert np.array_equal(got, np.sort(order[:c])), i
             assert (c == 1 or F[c - 2] < value + tol) and F[c - 1] >= value - tol, (i, c)
+
+
+@pytest.mark.parametrize("window_t", [32767, 32768, 70000])
+def test_window_radius_past_the_grid(vsa, window_t):
+    """A window radius at or beyond nbt - 1 keeps every temporal block: the
+    plan must equal the oracle's plan at that radius (every row holds every
+    key block) and record nbt - 1 in the index; a radius that does not fit
+    16 bits must not reach the selection kernel in a narrowed form."""
+    w = W.custom("bigwin", 1, 2, 64, (9, 10, 12), (4, 4, 8), "bf16", 0.2, -1, "smooth")
+    _say(f"[gpu] window radius {window_t}")
+    inp = W.generate(w, seed=71)
+    q, k = (_to_dev(inp[n], torch.bfloat16) for n in ("q", "k"))
+    g = O.geometry(w.grid, w.block)
+    idx = vsa.plan(q, k, w.grid, w.block, 0.2, window_t)
+    torch.cuda.synchronize()
+    rp, ci, _ = O.plan(inp["q"], inp["k"], w.grid, w.block, np.float32(0.2), window_t)
+    grp, gci = _index_np(idx)
+    assert np.array_equal(grp, rp) and np.array_equal(gci, ci)
+    assert np.all(np.diff(grp) == g.NB)
+    assert idx.window_t == g.nbt - 1
