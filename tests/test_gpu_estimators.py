@@ -104,14 +104,18 @@ def test_estimator_plan_and_attention(vsa, case):
     (rows, band, differ), (rp, ci) = check_index(grp, gci, S, g, mode, vals, window_t, sink, sc)
     ref = O.attention(inp["q"], inp["k"], inp["v"], w.grid, w.block, rp, ci)
     og = o.float().cpu().numpy()
-    skip = {int(r) for r in differ}
+    # A Top-P row inside the float32 band (its GPU cut was validated above)
+    # is checked against the oracle's attention over the GPU's own row.
+    own = {int(r) for r in differ}
     errs = []
     for r in range(rows):
-        if r in skip:
-            continue
         b, rem = divmod(r, w.heads * g.NB)
         h, i = divmod(rem, g.NB)
-        errs.append(np.abs(og[b, h, g.tokens[i]] - ref[b, h, g.tokens[i]]).ravel())
+        if r in own:
+            want = O.attention_row(inp["q"], inp["k"], inp["v"], g, grp, gci, b, h, i)
+        else:
+            want = ref[b, h, g.tokens[i]]
+        errs.append(np.abs(og[b, h, g.tokens[i]] - want).ravel())
     err = np.concatenate(errs)
     if w.dtype == "bf16":
         assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN, (err.max(), err.mean())
