@@ -30,7 +30,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "ms/attn call + executed TFLOP/s (% bf16 MFMA peak), Wan-1.3B shape, density 0.2"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
-PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector peak
+# fp32 vector peak without packed-fp32 instructions (the library is built
+# with them disabled): 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP (FMA) x 2.4 GHz.
+# The published 157.3 TFLOP/s counts packed fp32, which this build never issues.
+PEAK_F32_TFLOPS = 78.6
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_wan13b_traffic.txt")
 
@@ -92,8 +95,19 @@ def cpu_baseline(inp, w, row_ptr, col_idx, sizes, step_flops, budget_s=20.0):
     """The CPU oracle timed on the host: its full plan, plus its float64
     attention on a seeded sample of query blocks, scaled to a whole step."""
     from oracle import vsa_oracle as O
+    host_cores = len(os.sched_getaffinity(0))
+    cpu_model = "unknown"
     try:
-        from threadpoolctl import threadpool_info
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    limiter = None
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=host_cores)   # BLAS threads = every core this process may use
         cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
     except Exception:
         cores = 1
@@ -112,7 +126,10 @@ def cpu_baseline(inp, w, row_ptr, col_idx, sizes, step_flops, budget_s=20.0):
         f_attn += 4 * w.D * int(sizes[i]) * int(sizes[ci[rp[r]: rp[r + 1]]].sum())
         n_rows += 1
     t_step = t_plan + t_attn * (step_flops / max(f_attn, 1))
+    if limiter is not None:
+        limiter.restore_original_limits()
     return {"value": step_flops / t_step / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "host_cores": host_cores, "cpu_model": cpu_model,
             "sample": (f"full oracle plan ({t_plan:.2f} s) + float64 oracle attention on {n_rows} "
                        f"seeded query blocks ({t_attn:.1f} s, {f_attn / 1e9:.1f} GFLOP), scaled to "
                        f"the step's {step_flops / 1e12:.3f} TFLOP"),
@@ -266,6 +283,25 @@ def time_mixed(vsa, lib, _lib, q, k, v, o, w, stream, sizes, reps=20):
             "plan_ms": round(plan_ms, 4), "attn_ms": round(attn_ms, 4),
             "attn_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 2),
             "nnz_blocks": int(rp[-1]), "density": round(float(rp[-1]) / ((len(rp) - 1) * nb), 4)}
+
+
+def time_cold(attn_call, stream, reps=10, scratch_mib=512):
+    """Attention with cold caches: before every timed call a 512 MiB scratch
+    buffer is overwritten, which evicts K/V from L2 and the 256 MB Infinity
+    Cache; only the attention call sits between the events."""
+    import torch
+    scratch = torch.empty(scratch_mib << 20, dtype=torch.uint8, device="cuda")
+    ms = []
+    for r in range(reps):
+        scratch.fill_(r & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        attn_call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    del scratch
+    return float(np.median(ms))
 
 
 def main():
@@ -440,6 +476,11 @@ def main():
         # stores to raster order itself; these serve callers that want the
         # blocked layout), against the HBM roofline.
         result["layout"] = time_layout(vsa, lib, _lib, k, w, stream)
+    if not a.no_extras:
+        cold = time_cold(attn_call, stream)
+        result["attn_cold"] = {"scratch_MiB_between_calls": 512, "attn_ms_median": round(cold, 4),
+                               "attn_tflops": round(flops / (cold * 1e-3) / 1e12, 2),
+                               "warm_attn_ms": result["attn_ms"]}
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inp, w, rp, ci, sizes, flops, a.cpu_budget)
