@@ -23,7 +23,7 @@ import torch
 from . import _lib
 from ._lib import VsaError, VsaHeadOption, VsaIndex, VsaSelect, VsaShape, check, load
 
-__all__ = ["plan", "plan_select", "plan_mixed", "attn", "query", "query_select", "permute", "unpermute",
+__all__ = ["plan", "plan_noalloc", "plan_select", "plan_mixed", "attn", "query", "query_select", "permute", "unpermute",
            "centroids", "centroid_scores", "estimate", "sics", "select_scheme", "Index", "VsaError", "load"]
 
 _DTYPES = {torch.bfloat16: _lib.VSA_BF16, torch.float32: _lib.VSA_F32}
@@ -115,6 +115,33 @@ def plan(q: torch.Tensor, k: torch.Tensor, grid, block, density: Union[float, Se
                        ctypes.byref(shape), dens, nd, int(window_t), ctypes.byref(cidx),
                        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(q)), "vsa_plan")
     return Index(cidx.shape, cidx.nb, cidx.window_t, row_ptr, col_idx, cap, cidx.equal_heads)
+
+
+def plan_noalloc(q: torch.Tensor, k: torch.Tensor, grid, block, density: Union[float, Sequence[float]],
+                 window_t: int = -1, index: Optional[Index] = None) -> Index:
+    """plan() through vsa_plan_noalloc: the plan workspace comes from the
+    library's static per-GPU array, so the call allocates no workspace.
+    With `index` (an Index of the same shape, e.g. from an earlier call)
+    its arrays are reused and nothing at all is allocated."""
+    lib = load()
+    shape = _shape_of(q, grid, block)
+    if k.shape != q.shape or k.dtype != q.dtype or not k.is_contiguous():
+        raise ValueError("k must match q")
+    rl, cap, _, _ = query(shape, density, window_t)
+    if index is None:
+        row_ptr = torch.empty(rl, dtype=torch.int32, device=q.device)
+        col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=q.device)
+    else:
+        row_ptr, col_idx = index.row_ptr, index.col_idx
+        if row_ptr.numel() < rl or col_idx.numel() < cap or row_ptr.device != q.device:
+            raise ValueError("index arrays too small for this plan")
+    cidx = VsaIndex(shape, 0, 0, ctypes.c_void_p(row_ptr.data_ptr()), ctypes.c_void_p(col_idx.data_ptr()),
+                    col_idx.numel())
+    dens, nd = _densities(density, shape.heads)
+    check(lib.vsa_plan_noalloc(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                               ctypes.byref(shape), dens, nd, int(window_t), ctypes.byref(cidx), _stream(q)),
+          "vsa_plan_noalloc")
+    return Index(cidx.shape, cidx.nb, cidx.window_t, row_ptr, col_idx, cidx.capacity, cidx.equal_heads)
 
 
 _MODES = {"topk": _lib.VSA_TOPK, "topp": _lib.VSA_TOPP}

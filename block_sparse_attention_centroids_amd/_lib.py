@@ -29,6 +29,8 @@ VSA_HEAD_DYNAMIC = 0
 VSA_HEAD_STATIC = 1
 VSA_HEAD_DENSE = 2
 
+VSA_PLAN_NOALLOC_MAX_WS = 32 << 20
+
 
 class VsaShape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("heads", ctypes.c_int32), ("D", ctypes.c_int32),
@@ -64,7 +66,7 @@ _lib = None
 EXPORTS = ("vsa_query", "vsa_plan", "vsa_attn", "vsa_permute", "vsa_unpermute",
            "vsa_centroids", "vsa_centroid_scores", "vsa_sics", "vsa_scheme_workspace",
            "vsa_select_scheme", "vsa_query_select", "vsa_plan_select", "vsa_estimate", "vsa_query_mixed", "vsa_plan_mixed",
-           "vsa_status_str")
+           "vsa_plan_noalloc", "vsa_status_str")
 
 
 def load() -> ctypes.CDLL:
@@ -106,6 +108,8 @@ def load() -> ctypes.CDLL:
                                     ctypes.POINTER(ctypes.c_size_t)]
     lib.vsa_plan_mixed.argtypes = [P, P, ctypes.POINTER(VsaShape), ctypes.POINTER(VsaHeadOption), I, P,
                                    ctypes.POINTER(VsaIndex), P, ctypes.c_size_t, P]
+    lib.vsa_plan_noalloc.argtypes = [P, P, ctypes.POINTER(VsaShape), ctypes.POINTER(ctypes.c_float), I, I,
+                                     ctypes.POINTER(VsaIndex), P]
     for name in EXPORTS[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     lib.vsa_status_str.argtypes = [ctypes.c_int]

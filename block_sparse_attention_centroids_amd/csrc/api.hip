@@ -1,11 +1,13 @@
 // C ABI entry points (declared in include/vsa.h): host validation, then
 // kernel launches on the caller's stream.  No allocation, no device
-// synchronization, no global mutable state.
+// synchronization.  The only global state is the static plan workspace of
+// vsa_plan_noalloc and its per-device address table (end of this file).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "vsa.h"
 #include "vsa_host.h"
@@ -395,3 +397,61 @@ vsa_status vsa_select_scheme(const void* q, const void* k, const vsa_shape* shap
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Plan workspace for callers that cannot allocate: one static array per GPU.
+// In host code `scratch` names a host-side stand-in, not the device array;
+// kernels get the device address that hipGetSymbolAddress returns for the
+// device a call runs on, looked up once per device and kept.
+// ---------------------------------------------------------------------------
+static __device__ __attribute__((aligned(256))) unsigned char scratch[VSA_PLAN_NOALLOC_MAX_WS];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that `stream` belongs to (the
+// current device for the null stream).
+vsa_status scratch_address(hipStream_t stream, void** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return VSA_ERR_HIP;
+  int dev = cur;
+  if (stream != nullptr && hipStreamGetDevice(stream, &dev) != hipSuccess) return VSA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return VSA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return VSA_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return VSA_ERR_HIP;
+    if (e != hipSuccess || p == nullptr) return VSA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return VSA_OK;
+}
+
+}  // namespace
+
+extern "C" vsa_status vsa_plan_noalloc(const void* q, const void* k, const vsa_shape* shape,
+                                       const float* density, int n_density, int window_t, vsa_index* index,
+                                       void* stream) {
+  try {
+    if (!q || !k || !index) return VSA_ERR_INVALID_ARG;
+    PlanSizes ps;
+    vsa_status st = plan_sizes(shape, density, n_density, window_t, &ps);
+    if (st != VSA_OK) return st;
+    if (!index->row_ptr || !index->col_idx) return VSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k)) return VSA_ERR_INVALID_ARG;
+    if (index->capacity < ps.capacity) return VSA_ERR_CAPACITY;
+    if (ps.ws > VSA_PLAN_NOALLOC_MAX_WS) return VSA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    st = scratch_address(reinterpret_cast<hipStream_t>(stream), &ws);
+    if (st != VSA_OK) return st;
+    return run_plan(q, k, shape, ps, 0, 0, nullptr, index, ws, stream);
+  } catch (...) {
+    return VSA_ERR_INVALID_ARG;
+  }
+}

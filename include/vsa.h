@@ -33,8 +33,10 @@
  *   tokens.  Tokens inside a block are ordered row-major in (t, h, w).
  * Ownership.  The caller allocates every buffer (inputs, outputs, index
  *   arrays, workspace).  The library never allocates, never synchronizes the
- *   device and keeps no mutable global state; calls on different streams do
- *   not interfere unless they write the same buffers.
+ *   device and keeps no mutable global state, with one exception:
+ *   vsa_plan_noalloc takes its workspace from a static per-GPU array (see
+ *   there).  Calls on different streams do not interfere unless they write
+ *   the same buffers (or both are vsa_plan_noalloc calls on one GPU).
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = null stream).
  *   Work is only enqueued; results are valid once the caller has
  *   synchronized with the stream.
@@ -305,6 +307,29 @@ vsa_status vsa_scheme_workspace(const vsa_shape* shape, const int32_t* candidate
 vsa_status vsa_select_scheme(const void* q, const void* k, const vsa_shape* shape,
                              const int32_t* candidates, int n_cand, float* scores, int32_t* choice,
                              void* ws, size_t ws_bytes, void* stream);
+
+/* Largest plan workspace vsa_plan_noalloc holds (32 MiB per GPU). */
+#define VSA_PLAN_NOALLOC_MAX_WS ((size_t)32 << 20)
+
+/* vsa_plan for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same plan, bit for bit, with the plan workspace (block summaries and,
+ * for windowed plans, per-row counts and bitmaps) taken from a static
+ * device array of VSA_PLAN_NOALLOC_MAX_WS bytes inside the library instead
+ * of a caller buffer.  Each GPU the library runs on holds its own copy of
+ * the array until the process ends; its address is looked up once per
+ * device, on the first call that runs there.  The caller still owns q, k
+ * and the index arrays.  A plan whose workspace (plan_ws of vsa_query)
+ * exceeds VSA_PLAN_NOALLOC_MAX_WS returns VSA_ERR_WORKSPACE before anything
+ * is enqueued; the Wan2.1-1.3B, HunyuanVideo, Wan2.1-14B and 4x long-video
+ * shapes need 4.1, 11.8, 13.8 and 16.6 MB.  No call allocates or frees
+ * device memory.  Every call on one GPU shares that GPU's array, and every
+ * value a plan reads from it is written earlier in the same call, so
+ * nothing has to start at zero; two calls that overlap in time on one GPU
+ * (different streams, or host threads) race on the array and must be
+ * ordered by the caller.  Other arguments as in vsa_plan. */
+vsa_status vsa_plan_noalloc(const void* q, const void* k, const vsa_shape* shape, const float* density,
+                            int n_density, int window_t, vsa_index* index, void* stream);
 
 /* Static description of a status code. */
 const char* vsa_status_str(vsa_status s);
