@@ -84,12 +84,17 @@ inline vsa_status check_shape(const vsa_shape* s) {
   int64_t bt = std::min(s->bt, s->T), bh = std::min(s->bh, s->H), bw = std::min(s->bw, s->W);
   if (bt * bh * bw > VSA_MAX_BLOCK_TOKENS) return VSA_ERR_UNSUPPORTED;
   (void)box;
-  int64_t N = int64_t(s->T) * s->H * s->W;
+  // Products are bounded step by step so that none can overflow int64.
+  const int64_t TH = int64_t(s->T) * s->H;   // < 2^62
+  if (TH > (int64_t(1) << 30)) return VSA_ERR_UNSUPPORTED;
+  const int64_t N = TH * s->W;               // < 2^61
   if (N > (int64_t(1) << 30)) return VSA_ERR_UNSUPPORTED;
   // One head's tensor must be addressable with 32-bit byte offsets.
-  if (N * s->D * elt_bytes(s->dtype) >= (int64_t(1) << 31)) return VSA_ERR_UNSUPPORTED;
-  int64_t elems = int64_t(s->B) * s->heads * N * s->D;
-  if (elems > (int64_t(1) << 40)) return VSA_ERR_UNSUPPORTED;
+  const int64_t per_head = N * s->D;         // < 2^38
+  if (per_head * elt_bytes(s->dtype) >= (int64_t(1) << 31)) return VSA_ERR_UNSUPPORTED;
+  // B * heads * N * D <= 2^40 elements.
+  const int64_t BH = int64_t(s->B) * s->heads;   // < 2^62
+  if (BH > (int64_t(1) << 40) / per_head) return VSA_ERR_UNSUPPORTED;
   Geo g = make_geo(*s);
   if (g.NB > 16384) return VSA_ERR_UNSUPPORTED;
   if (int64_t(s->B) * s->heads * g.NB >= (int64_t(1) << 31) - 1) return VSA_ERR_UNSUPPORTED;
