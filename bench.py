@@ -285,6 +285,43 @@ def time_mixed(vsa, lib, _lib, q, k, v, o, w, stream, sizes, reps=20):
             "nnz_blocks": int(rp[-1]), "density": round(float(rp[-1]) / ((len(rp) - 1) * nb), 4)}
 
 
+def time_scheme_flow(vsa, q, k, w, cands, dens, stream, plan_ms, reps=10):
+    """Scheme selection that keeps each candidate's block means, then the
+    plan of every head at the chosen candidate from those means (Q and K
+    are read once per candidate in all), against selection plus a plan that
+    reads Q and K again."""
+    import torch
+    for _ in range(2):
+        _, choice, sm = vsa.select_scheme_means(q, k, w.grid, cands)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        _, choice, sm = vsa.select_scheme_means(q, k, w.grid, cands)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sel_ms = e0.elapsed_time(e1) / reps
+    c = int(choice[0].item())
+    heads = list(range(w.heads))
+    qm, km = sm.means(c)
+    for _ in range(2):
+        vsa.plan_heads(None, None, w.grid, cands[c], heads, dens[0], w.window_t, means=(qm, km),
+                       heads_total=w.heads, B=w.B, D=w.D)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        vsa.plan_heads(None, None, w.grid, cands[c], heads, dens[0], w.window_t, means=(qm, km),
+                       heads_total=w.heads, B=w.B, D=w.D)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    plan_means_ms = e0.elapsed_time(e1) / reps
+    tensor_bytes = 2 * q.numel() * q.element_size()
+    return {"select_with_means_ms": round(sel_ms, 4), "plan_from_means_ms": round(plan_means_ms, 4),
+            "plan_reading_qk_ms": round(float(plan_ms), 4),
+            "bytes_select_then_plan": (len(cands) + 1) * tensor_bytes,
+            "bytes_with_means": len(cands) * tensor_bytes}
+
+
 def time_cold(attn_call, stream, reps=10, scratch_mib=512):
     """Attention with cold caches: before every timed call a 512 MiB scratch
     buffer is overwritten, which evicts K/V from L2 and the 256 MB Infinity
@@ -463,6 +500,7 @@ def main():
             "algorithmic_bytes": sel_bytes, "GB_per_s": round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(sel_bytes / (sel_ms * 1e-3) / 8e12, 4),
             "choices": choice.cpu().tolist()}
+        result["scheme_means_flow"] = time_scheme_flow(vsa, q, k, w, cands, dens, stream, plan_ms.mean())
     # Selection variants (outside the timed step): Top-P and Top-K with
     # attention-sink blocks, each planned in place into preallocated buffers
     # and followed by attention over the index it produced.

@@ -23,7 +23,8 @@ import torch
 from . import _lib
 from ._lib import VsaError, VsaHeadOption, VsaIndex, VsaSelect, VsaShape, check, load
 
-__all__ = ["plan", "plan_noalloc", "plan_select", "plan_mixed", "attn", "query", "query_select", "permute", "unpermute",
+__all__ = ["plan", "plan_noalloc", "plan_heads", "attn_heads", "select_scheme_means", "plan_schemes",
+           "attn_schemes", "SchemeMeans", "SchemePlan", "plan_select", "plan_mixed", "attn", "query", "query_select", "permute", "unpermute",
            "centroids", "centroid_scores", "estimate", "sics", "select_scheme", "Index", "VsaError", "load"]
 
 _DTYPES = {torch.bfloat16: _lib.VSA_BF16, torch.float32: _lib.VSA_F32}
@@ -396,3 +397,167 @@ def select_scheme(q: torch.Tensor, k: torch.Tensor, grid, candidates: Sequence[S
                                 cand, n, ctypes.c_void_p(scores.data_ptr()), ctypes.c_void_p(choice.data_ptr()),
                                 ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(q)), "vsa_select_scheme")
     return scores, choice
+
+
+# ---------------------------------------------------------------------------
+# Per-head blocking schemes: calls over a subset of the heads, and scheme
+# selection that keeps each candidate's block means for the plans after it.
+# ---------------------------------------------------------------------------
+
+def _head_list(heads):
+    hl = [int(h) for h in heads]
+    return (ctypes.c_int32 * len(hl))(*hl), len(hl)
+
+
+def plan_heads(q: Optional[torch.Tensor], k: Optional[torch.Tensor], grid, block, heads: Sequence[int],
+               density: Union[float, Sequence[float]], window_t: int = -1,
+               means: Optional[Tuple[torch.Tensor, torch.Tensor]] = None, heads_total: Optional[int] = None,
+               B: Optional[int] = None, D: Optional[int] = None, dtype=torch.bfloat16) -> Index:
+    """Plan of the listed heads of q, k ([B, total, N, D]) under one
+    blocking.  With means = (query means, key means) of every head (as
+    select_scheme_means leaves them) q and k are not read; then heads_total,
+    B, D and dtype describe the tensors when q is None.  density: one value
+    or one per listed head."""
+    lib = load()
+    if q is not None:
+        shape = _shape_of(q, grid, block)
+        if k is None or k.shape != q.shape or k.dtype != q.dtype or not k.is_contiguous():
+            raise ValueError("k must match q")
+        dev = q.device
+    else:
+        if means is None:
+            raise ValueError("q and k, or means, are needed")
+        T, H, W = (int(a) for a in grid)
+        shape = VsaShape(int(B), int(heads_total), int(D), T, H, W, *(int(a) for a in block), _DTYPES[dtype])
+        dev = means[0].device
+    hl, n = _head_list(heads)
+    sub = VsaShape(shape.B, n, shape.D, shape.T, shape.H, shape.W, shape.bt, shape.bh, shape.bw, shape.dtype)
+    rl, cap, pws, _ = query(sub, density, window_t)
+    row_ptr = torch.empty(rl, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(pws, 1), dtype=torch.uint8, device=dev)
+    cidx = VsaIndex(sub, 0, 0, ctypes.c_void_p(row_ptr.data_ptr()), ctypes.c_void_p(col_idx.data_ptr()), cap)
+    dens, nd = _densities(density, n)
+    ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    qm, km = (None, None) if means is None else means
+    if means is not None:
+        for t in (qm, km):
+            if t.dtype != torch.float32 or not t.is_contiguous() or t.device != dev:
+                raise ValueError("means must be contiguous float32 tensors on the device")
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    check(lib.vsa_plan_heads(ptr(q), ptr(k), ptr(qm), ptr(km), ctypes.byref(shape), hl, n, dens, nd, int(window_t),
+                             ctypes.byref(cidx), ctypes.c_void_p(ws.data_ptr()), ws.numel(), stream),
+          "vsa_plan_heads")
+    return Index(cidx.shape, cidx.nb, cidx.window_t, row_ptr, col_idx, cap, cidx.equal_heads)
+
+
+def attn_heads(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, index: Index, heads: Sequence[int],
+               out: Optional[torch.Tensor] = None, scale: Optional[float] = None) -> torch.Tensor:
+    """Attention of the listed heads (the index's row order) into out (a
+    zero tensor like q when None); the other heads of out are left as
+    they are."""
+    lib = load()
+    _shape_of(q, index.grid, index.block)
+    for t in (k, v):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("q, k, v must share shape, dtype and be contiguous")
+    o = torch.zeros_like(q) if out is None else out
+    if out is not None:
+        _check_out(q, out)
+    hl, n = _head_list(heads)
+    if n != index.shape.heads:
+        raise ValueError("the head list must have one entry per head of the index")
+    cidx = index.c_index()
+    check(lib.vsa_attn_heads(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                             ctypes.c_void_p(v.data_ptr()), ctypes.byref(cidx), hl, int(q.shape[1]),
+                             ctypes.c_float(0.0 if scale is None else float(scale)), ctypes.c_void_p(o.data_ptr()),
+                             None, 0, _stream(q)), "vsa_attn_heads")
+    return o
+
+
+@dataclass
+class SchemeMeans:
+    """Workspace of select_scheme_means: each candidate's block means of Q
+    ([B*heads, NB_c, D]) and K ([B*heads, D, NB_c]) stay in it."""
+    ws: torch.Tensor
+    offsets: Tuple[int, ...]
+    candidates: Tuple[Tuple[int, int, int], ...]
+    grid: Tuple[int, int, int]
+    B: int
+    heads: int
+    D: int
+
+    def means(self, c: int) -> Tuple[torch.Tensor, torch.Tensor]:
+        nb = math.prod(-(-int(n) // int(b)) for n, b in zip(self.grid, self.candidates[c]))
+        cnt = self.B * self.heads * nb * self.D
+        qm = self.ws[self.offsets[2 * c]: self.offsets[2 * c] + 4 * cnt].view(torch.float32)
+        km = self.ws[self.offsets[2 * c + 1]: self.offsets[2 * c + 1] + 4 * cnt].view(torch.float32)
+        return qm, km
+
+
+def select_scheme_means(q: torch.Tensor, k: torch.Tensor, grid, candidates: Sequence[Sequence[int]]):
+    """select_scheme that also keeps each candidate's block means: returns
+    (scores [n_cand, B*heads], choice [B*heads], SchemeMeans)."""
+    lib = load()
+    s = _shape_of(q, grid, candidates[0])
+    if k.shape != q.shape or k.dtype != q.dtype or not k.is_contiguous():
+        raise ValueError("k must match q")
+    flat = [int(a) for c in candidates for a in c]
+    if len(flat) != 3 * len(candidates):
+        raise ValueError("each candidate is a (bt, bh, bw) triple")
+    cand = (ctypes.c_int32 * len(flat))(*flat)
+    n = len(candidates)
+    wsb = ctypes.c_size_t()
+    offs = (ctypes.c_size_t * (2 * n))()
+    check(lib.vsa_scheme_means_workspace(ctypes.byref(s), cand, n, ctypes.byref(wsb), offs),
+          "vsa_scheme_means_workspace")
+    ws = torch.empty(max(int(wsb.value), 1), dtype=torch.uint8, device=q.device)
+    bh = s.B * s.heads
+    scores = torch.empty((n, bh), dtype=torch.float32, device=q.device)
+    choice = torch.empty((bh,), dtype=torch.int32, device=q.device)
+    check(lib.vsa_select_scheme_means(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                                      ctypes.byref(s), cand, n, ctypes.c_void_p(scores.data_ptr()),
+                                      ctypes.c_void_p(choice.data_ptr()), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                      _stream(q)), "vsa_select_scheme_means")
+    sm = SchemeMeans(ws, tuple(int(x) for x in offs), tuple(tuple(int(a) for a in c) for c in candidates),
+                     tuple(int(a) for a in grid), s.B, s.heads, s.D)
+    return scores, choice, sm
+
+
+@dataclass
+class SchemePlan:
+    """Per-head plan: for every candidate chosen by some head, the heads
+    that chose it and their index under that blocking."""
+    groups: list            # [(candidate index, block, [heads], Index)]
+    scores: torch.Tensor
+    choice: torch.Tensor
+
+
+def plan_schemes(q: torch.Tensor, k: torch.Tensor, grid, candidates: Sequence[Sequence[int]],
+                 density: float, window_t: int = -1) -> SchemePlan:
+    """Head-wise blocking schemes end to end: select_scheme_means, then one
+    plan per chosen candidate over the heads that chose it, from the means
+    the selection left (Q and K are read once per candidate in all).  The
+    heads' choices come back to the host to group them (one sync).  With
+    B > 1 a head's scheme is taken from batch item 0."""
+    scores, choice, sm = select_scheme_means(q, k, grid, candidates)
+    ch = choice.cpu().tolist()[: q.shape[1]]
+    groups = []
+    for c in range(len(candidates)):
+        hs = [h for h in range(q.shape[1]) if ch[h] == c]
+        if not hs:
+            continue
+        idx = plan_heads(None, None, grid, candidates[c], hs, density, window_t, means=sm.means(c),
+                         heads_total=q.shape[1], B=q.shape[0], D=q.shape[3], dtype=q.dtype)
+        groups.append((c, tuple(int(a) for a in candidates[c]), hs, idx))
+    return SchemePlan(groups, scores, choice)
+
+
+def attn_schemes(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sp: SchemePlan,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Attention of every head under its own blocking scheme, one launch per
+    group of heads that share a scheme, into one output."""
+    o = torch.empty_like(q) if out is None else out
+    for _, _, hs, idx in sp.groups:
+        attn_heads(q, k, v, idx, hs, out=o)
+    return o

@@ -66,7 +66,8 @@ _lib = None
 EXPORTS = ("vsa_query", "vsa_plan", "vsa_attn", "vsa_permute", "vsa_unpermute",
            "vsa_centroids", "vsa_centroid_scores", "vsa_sics", "vsa_scheme_workspace",
            "vsa_select_scheme", "vsa_query_select", "vsa_plan_select", "vsa_estimate", "vsa_query_mixed", "vsa_plan_mixed",
-           "vsa_plan_noalloc", "vsa_status_str")
+           "vsa_plan_noalloc", "vsa_plan_heads", "vsa_attn_heads", "vsa_scheme_means_workspace",
+           "vsa_select_scheme_means", "vsa_status_str")
 
 
 def load() -> ctypes.CDLL:
@@ -110,6 +111,15 @@ def load() -> ctypes.CDLL:
                                    ctypes.POINTER(VsaIndex), P, ctypes.c_size_t, P]
     lib.vsa_plan_noalloc.argtypes = [P, P, ctypes.POINTER(VsaShape), ctypes.POINTER(ctypes.c_float), I, I,
                                      ctypes.POINTER(VsaIndex), P]
+    lib.vsa_plan_heads.argtypes = [P, P, P, P, ctypes.POINTER(VsaShape), ctypes.POINTER(ctypes.c_int32), I,
+                                   ctypes.POINTER(ctypes.c_float), I, I, ctypes.POINTER(VsaIndex), P,
+                                   ctypes.c_size_t, P]
+    lib.vsa_attn_heads.argtypes = [P, P, P, ctypes.POINTER(VsaIndex), ctypes.POINTER(ctypes.c_int32), I,
+                                   ctypes.c_float, P, P, ctypes.c_size_t, P]
+    lib.vsa_scheme_means_workspace.argtypes = [ctypes.POINTER(VsaShape), ctypes.POINTER(ctypes.c_int32), I,
+                                               ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
+    lib.vsa_select_scheme_means.argtypes = [P, P, ctypes.POINTER(VsaShape), ctypes.POINTER(ctypes.c_int32), I, P,
+                                            P, P, ctypes.c_size_t, P]
     for name in EXPORTS[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     lib.vsa_status_str.argtypes = [ctypes.c_int]

@@ -40,22 +40,60 @@ vsa_status hip_status(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_
 
 // Enqueue the block summaries of the estimator into the workspace regions
 // ps.off_sum and describe them for the scoring kernels.
+// With qmeans/kmeans (the block means of every tensor head, as
+// vsa_select_scheme_means leaves them), the means of the call's heads are
+// gathered from there instead of being computed from q and k.
 hipError_t summarize(const void* q, const void* k, const vsa_shape* shape, const PlanSizes& ps, char* w,
-                     const DGeo& dg, int BH, hipStream_t st, Summaries* sm) {
+                     const DGeo& dg, int BH, hipStream_t st, Summaries* sm, const HeadMap* hm = nullptr,
+                     const float* qmeans = nullptr, const float* kmeans = nullptr) {
   float* s0 = reinterpret_cast<float*>(w + ps.off_sum[0]);
   float* s1 = reinterpret_cast<float*>(w + ps.off_sum[1]);
   float* s2 = ps.n_sum > 2 ? reinterpret_cast<float*>(w + ps.off_sum[2]) : nullptr;
   float* s3 = ps.n_sum > 3 ? reinterpret_cast<float*>(w + ps.off_sum[3]) : nullptr;
   if (ps.estimator == VSA_EST_MEAN) {
     *sm = Summaries{s0, nullptr, s1, nullptr, 1};
-    return launch_pool(q, s0, k, s1, shape->dtype, shape->D, dg, BH, st, true);
+    if (qmeans) {
+      const HeadMap id;
+      const HeadMap& m = hm ? *hm : id;
+      hipError_t e = launch_gather_rows(qmeans, s0, dg.NB * shape->D, m, BH, st);
+      if (e == hipSuccess) e = launch_gather_rows(kmeans, s1, dg.NB * shape->D, m, BH, st);
+      return e;
+    }
+    return launch_pool(q, s0, k, s1, shape->dtype, shape->D, dg, BH, st, true, hm);
   }
   if (ps.estimator == VSA_EST_DSA) {
     *sm = Summaries{s0, nullptr, s1, s2, 1};
-    return launch_extremes(q, s0, nullptr, 1, k, s1, s2, 0, shape->dtype, shape->D, dg, BH, st, true);
+    return launch_extremes(q, s0, nullptr, 1, k, s1, s2, 0, shape->dtype, shape->D, dg, BH, st, true, hm);
   }
   *sm = Summaries{s0, s1, s2, s3, 1};
-  return launch_extremes(q, s0, s1, 0, k, s2, s3, 0, shape->dtype, shape->D, dg, BH, st, true);
+  return launch_extremes(q, s0, s1, 0, k, s2, s3, 0, shape->dtype, shape->D, dg, BH, st, true, hm);
+}
+
+// Head list of a call over tensors with `total` heads: n distinct heads,
+// each in [0, total), at most VSA_MAX_HEADS.
+vsa_status make_head_map(const int32_t* heads, int n, int total, HeadMap* hm) {
+  if (!heads || n < 1 || total < 1 || n > total) return VSA_ERR_INVALID_ARG;
+  if (n > VSA_MAX_HEADS) return VSA_ERR_UNSUPPORTED;
+  if (total > 32767) return VSA_ERR_UNSUPPORTED;
+  bool seen[VSA_MAX_HEADS] = {};
+  bool identity = n == total;
+  for (int s2 = 0; s2 < n; ++s2) {
+    const int h = heads[s2];
+    if (h < 0 || h >= total) return VSA_ERR_INVALID_ARG;
+    if (h < VSA_MAX_HEADS) {
+      if (seen[h]) return VSA_ERR_INVALID_ARG;
+      seen[h] = true;
+    } else {
+      for (int t = 0; t < s2; ++t)
+        if (heads[t] == h) return VSA_ERR_INVALID_ARG;
+    }
+    hm->h[s2] = static_cast<int16_t>(h);
+    identity = identity && h == s2;
+  }
+  hm->n = n;
+  hm->total = total;
+  hm->identity = identity ? 1 : 0;
+  return VSA_OK;
 }
 
 }  // namespace
@@ -114,7 +152,8 @@ namespace {
 // (when a head is dynamic), scoring + selection, then scan + fill when rows
 // vary in length.  Everything the host can check has been checked.
 vsa_status run_plan(const void* q, const void* k, const vsa_shape* shape, const PlanSizes& ps, int topp,
-                    int sink, const float* table, vsa_index* index, void* ws, void* stream) {
+                    int sink, const float* table, vsa_index* index, void* ws, void* stream,
+                    const HeadMap* hm = nullptr, const float* qmeans = nullptr, const float* kmeans = nullptr) {
   const Geo g = make_geo(*shape);
   const DGeo dg = to_dgeo(g);
   const int BH = shape->B * shape->heads;
@@ -155,7 +194,7 @@ vsa_status run_plan(const void* q, const void* k, const vsa_shape* shape, const 
 
   Summaries sm{nullptr, nullptr, nullptr, nullptr};
   hipError_t e = hipSuccess;
-  if (ps.any_dynamic) e = summarize(q, k, shape, ps, w, dg, BH, st_, &sm);
+  if (ps.any_dynamic) e = summarize(q, k, shape, ps, w, dg, BH, st_, &sm, hm, qmeans, kmeans);
   if (e == hipSuccess)
     e = launch_score_select(sm, ps.estimator, dg, shape->D, shape->heads, BH, sa, index->row_ptr,
                             index->col_idx, counts, bits, st_);
@@ -397,6 +436,137 @@ vsa_status vsa_select_scheme(const void* q, const void* k, const vsa_shape* shap
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Calls over a subset of the heads, and scheme selection that keeps each
+// candidate's block means for the plans that follow it.
+// ---------------------------------------------------------------------------
+extern "C" vsa_status vsa_plan_heads(const void* q, const void* k, const float* qmeans, const float* kmeans,
+                                     const vsa_shape* shape, const int32_t* heads, int n_heads,
+                                     const float* density, int n_density, int window_t, vsa_index* index,
+                                     void* ws, size_t ws_bytes, void* stream) {
+  try {
+    if (!shape || !index) return VSA_ERR_INVALID_ARG;
+    HeadMap hm;
+    vsa_status st = check_shape(shape);
+    if (st != VSA_OK) return st;
+    st = make_head_map(heads, n_heads, shape->heads, &hm);
+    if (st != VSA_OK) return st;
+    vsa_shape cs = *shape;
+    cs.heads = n_heads;
+    PlanSizes ps;
+    st = plan_sizes(&cs, density, n_density, window_t, &ps);
+    if (st != VSA_OK) return st;
+    const bool from_means = qmeans != nullptr || kmeans != nullptr;
+    if (from_means) {
+      if (!qmeans || !kmeans || !aligned16(qmeans) || !aligned16(kmeans)) return VSA_ERR_INVALID_ARG;
+    } else if (!q || !k || !aligned16(q) || !aligned16(k)) {
+      return VSA_ERR_INVALID_ARG;
+    }
+    if (!index->row_ptr || !index->col_idx || !ws || !aligned16(ws)) return VSA_ERR_INVALID_ARG;
+    if (index->capacity < ps.capacity) return VSA_ERR_CAPACITY;
+    if (ws_bytes < ps.ws) return VSA_ERR_WORKSPACE;
+    return run_plan(q, k, &cs, ps, 0, 0, nullptr, index, ws, stream, &hm, qmeans, kmeans);
+  } catch (...) {
+    return VSA_ERR_INVALID_ARG;
+  }
+}
+
+extern "C" vsa_status vsa_attn_heads(const void* q, const void* k, const void* v, const vsa_index* index,
+                                     const int32_t* heads, int heads_total, float scale, void* o, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!q || !k || !v || !o || !index) return VSA_ERR_INVALID_ARG;
+  if (!index->row_ptr || !index->col_idx) return VSA_ERR_INVALID_ARG;
+  vsa_status st = check_shape(&index->shape);
+  if (st != VSA_OK) return st;
+  HeadMap hm;
+  st = make_head_map(heads, index->shape.heads, heads_total, &hm);
+  if (st != VSA_OK) return st;
+  vsa_shape full = index->shape;
+  full.heads = heads_total;
+  st = check_shape(&full);
+  if (st != VSA_OK) return st;
+  const Geo g = make_geo(index->shape);
+  if (index->nb != g.NB || index->window_t < -1) return VSA_ERR_SHAPE_MISMATCH;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return VSA_ERR_INVALID_ARG;
+  if (scale == 0.0f) scale = 1.0f / std::sqrt(static_cast<float>(index->shape.D));
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return VSA_ERR_INVALID_ARG;
+  const int BH = index->shape.B * index->shape.heads;
+  return hip_status(launch_attn(q, k, v, o, index->shape.dtype, index->shape.D, index->row_ptr, index->col_idx,
+                                to_dgeo(g), BH, scale, index->equal_heads != 0,
+                                reinterpret_cast<hipStream_t>(stream), &hm));
+}
+
+// Layout of vsa_select_scheme_means' workspace: the SICS regions of
+// scheme_layout, then per candidate the query means [B*heads][nb][D] and the
+// key means [B*heads][D][nb], each 256-byte aligned.
+static vsa_status scheme_means_layout(const vsa_shape* shape, const int32_t* cand, int n_cand,
+                                      vsa::SchemeArgs* sa, size_t* means_off, size_t* bytes) {
+  size_t off = 0;
+  vsa_status st = scheme_layout(shape, cand, n_cand, sa, &off);
+  if (st != VSA_OK) return st;
+  const size_t BH = (size_t)shape->B * shape->heads;
+  for (int c = 0; c < n_cand; ++c) {
+    vsa_shape s = *shape;
+    s.bt = cand[3 * c];
+    s.bh = cand[3 * c + 1];
+    s.bw = cand[3 * c + 2];
+    const Geo g = make_geo(s);
+    const size_t one = align256(BH * g.NB * shape->D * sizeof(float));
+    if (means_off) {
+      means_off[2 * c] = off;
+      means_off[2 * c + 1] = off + one;
+    }
+    off += 2 * one;
+  }
+  if (bytes) *bytes = off;
+  return VSA_OK;
+}
+
+extern "C" vsa_status vsa_scheme_means_workspace(const vsa_shape* shape, const int32_t* candidates, int n_cand,
+                                                 size_t* ws_bytes, size_t* means_off) {
+  try {
+    return scheme_means_layout(shape, candidates, n_cand, nullptr, means_off, ws_bytes);
+  } catch (...) {
+    return VSA_ERR_INVALID_ARG;
+  }
+}
+
+extern "C" vsa_status vsa_select_scheme_means(const void* q, const void* k, const vsa_shape* shape,
+                                              const int32_t* candidates, int n_cand, float* scores, int32_t* choice,
+                                              void* ws, size_t ws_bytes, void* stream) {
+  try {
+    vsa::SchemeArgs sa{};
+    size_t need = 0;
+    size_t moff[2 * VSA_MAX_SCHEMES];
+    vsa_status st = scheme_means_layout(shape, candidates, n_cand, &sa, moff, &need);
+    if (st != VSA_OK) return st;
+    if (!q || !k || !scores || !choice || !ws || !aligned16(q) || !aligned16(k) || !aligned16(ws))
+      return VSA_ERR_INVALID_ARG;
+    if (ws_bytes < need) return VSA_ERR_WORKSPACE;
+    hipStream_t st_ = reinterpret_cast<hipStream_t>(stream);
+    const int BH = shape->B * shape->heads;
+    char* w = static_cast<char*>(ws);
+    float* sics = static_cast<float*>(ws);
+    for (int c = 0; c < n_cand; ++c) {
+      vsa_shape s = *shape;
+      s.bt = candidates[3 * c];
+      s.bh = candidates[3 * c + 1];
+      s.bw = candidates[3 * c + 2];
+      const Geo g = make_geo(s);
+      float* base = sics + sa.off[c];
+      const hipError_t e = launch_pool_sics(q, reinterpret_cast<float*>(w + moff[2 * c]), k,
+                                            reinterpret_cast<float*>(w + moff[2 * c + 1]), base,
+                                            base + (size_t)BH * g.NB, shape->dtype, shape->D, to_dgeo(g), BH, st_);
+      if (e != hipSuccess) return VSA_ERR_HIP;
+    }
+    return hip_status(launch_scheme_select(sics, sa, BH, scores, choice, st_));
+  } catch (...) {
+    return VSA_ERR_INVALID_ARG;
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Plan workspace for callers that cannot allocate: one static array per GPU.

@@ -174,7 +174,7 @@ template <int D>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
-    DGeo g, float scale_log2, int contiguous) {
+    DGeo g, float scale_log2, int contiguous, HeadMap hm) {
   using C = AttnCfg<D>;
   constexpr int PARTS = C::PARTS, IPW = C::IPW, ROW = C::ROW, TILE = C::TILE;
   constexpr int RPI = C::ROWS_PER_INST;
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int ni = bi.n();
   TokenMap qmap;
   qmap.init(g, bi);
-  const size_t head_off = (size_t)bh * g.N * D;
+  const size_t head_off = (size_t)hm.tensor_bh(bh) * g.N * D;   // rows index the call's heads
   const uint32_t head_bytes = (uint32_t)g.N * D * 2u;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc4(k + head_off, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc4(v + head_off, head_bytes);
@@ -654,7 +654,7 @@ template <int D>
 __global__ __launch_bounds__(128) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
-    DGeo g, float scale) {
+    DGeo g, float scale, HeadMap hm) {
   constexpr int TK = 32;
   constexpr int SK = D == 64 ? 16 : 4;   // keys per score group (registers: q, o and the group's scores)
   static_assert(TK % SK == 0, "a score group must not run past the tile");
@@ -666,7 +666,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
   const int ni = bi.n();
   TokenMap qmap;
   qmap.init(g, bi);
-  const size_t head_off = (size_t)bh * g.N * D;
+  const size_t head_off = (size_t)hm.tensor_bh(bh) * g.N * D;
   const bool active = tid < ni;
   float qv[D], ov[D];
   const float* qp = q + head_off + (size_t)(active ? qmap(tid) : 0) * D;
@@ -757,24 +757,26 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
 
 hipError_t launch_attn(const void* q, const void* k, const void* v, void* o, int dtype, int D,
                        const int32_t* row_ptr, const int32_t* col_idx, const DGeo& g, int BH,
-                       float scale, bool contiguous, hipStream_t st) {
+                       float scale, bool contiguous, hipStream_t st, const HeadMap* hm) {
+  const HeadMap id;
+  const HeadMap& m = hm ? *hm : id;
   const unsigned nwg = (unsigned)BH * (unsigned)g.NB;
   if (dtype == VSA_BF16) {
     const float sl2 = scale * 1.4426950408889634f;
     const int cont = contiguous ? 1 : 0;
     if (D == 128)
       hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(nwg), dim3(THREADS), 0, st, (const uint16_t*)q,
-                         (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, row_ptr, col_idx, g, sl2, cont);
+                         (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, row_ptr, col_idx, g, sl2, cont, m);
     else
       hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(nwg), dim3(THREADS), 0, st, (const uint16_t*)q,
-                         (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, row_ptr, col_idx, g, sl2, cont);
+                         (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, row_ptr, col_idx, g, sl2, cont, m);
   } else {
     if (D == 128)
       hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(nwg), dim3(128), 0, st, (const float*)q,
-                         (const float*)k, (const float*)v, (float*)o, row_ptr, col_idx, g, scale);
+                         (const float*)k, (const float*)v, (float*)o, row_ptr, col_idx, g, scale, m);
     else
       hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(nwg), dim3(128), 0, st, (const float*)q,
-                         (const float*)k, (const float*)v, (float*)o, row_ptr, col_idx, g, scale);
+                         (const float*)k, (const float*)v, (float*)o, row_ptr, col_idx, g, scale, m);
   }
   return hipGetLastError();
 }

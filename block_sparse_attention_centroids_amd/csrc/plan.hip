@@ -33,17 +33,29 @@ namespace vsa {
 // ---------------------------------------------------------------------------
 __device__ inline int uniform_i(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-template <typename T, int D, bool EXT>
+template <typename T, int D, bool EXT, bool SICS>
 __global__ __launch_bounds__(256) void summary_kernel(const T* __restrict__ x0, float* __restrict__ oa0,
                                                       float* __restrict__ ob0, int mid0,
                                                       const T* __restrict__ x1, float* __restrict__ oa1,
-                                                      float* __restrict__ ob1, int mid1, DGeo g, int cm1) {
+                                                      float* __restrict__ ob1, int mid1, DGeo g, int cm1,
+                                                      float* __restrict__ sc0, float* __restrict__ sc1,
+                                                      HeadMap hm) {
   constexpr int ROWB = D * (int)sizeof(T);
   constexpr int PIECES = ROWB / 16;
   extern __shared__ uint4 stage16[];   // the block's tokens, [n][D] of T (room for 128)
   const T* stage = reinterpret_cast<const T*>(stage16);
-  const int item = blockIdx.x;         // bh * NB + j
-  const bool second = blockIdx.y != 0;
+  // Workgroups are dealt round-robin to the 8 XCDs by linear id; each XCD
+  // takes one contiguous run of (tensor, bh, block) items instead, so the
+  // channel-major 4-byte stores of neighbouring key blocks meet in one
+  // XCD's L2 and leave it as whole lines.
+  const int nit = (int)gridDim.x;
+  const int total = nit * (int)gridDim.y;
+  const int lin = (int)blockIdx.y * nit + (int)blockIdx.x;
+  const int xcd = lin & 7, loc = lin >> 3;
+  const int per = (total + 7) >> 3, rem8 = total & 7;
+  const int logical = (rem8 == 0 || xcd < rem8) ? xcd * per + loc : rem8 * per + (xcd - rem8) * (per - 1) + loc;
+  const bool second = logical >= nit;
+  const int item = second ? logical - nit : logical;   // bh * NB + j
   const T* x = second ? x1 : x0;
   float* oa = second ? oa1 : oa0;
   float* ob = second ? ob1 : ob0;
@@ -53,7 +65,7 @@ __global__ __launch_bounds__(256) void summary_kernel(const T* __restrict__ x0, 
   const int n = b.n();
   TokenMap map;
   map.init(g, b);
-  const uint8_t* src = reinterpret_cast<const uint8_t*>(x) + (size_t)bh * g.N * ROWB;
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(x) + (size_t)hm.tensor_bh(bh) * g.N * ROWB;
   // Every piece a thread copies is loaded before any is stored, so the
   // loads are all in flight together.  Loads and stores are unconditional,
   // so no branch splits them: a slot past the block's last piece re-reads
@@ -70,33 +82,108 @@ __global__ __launch_bounds__(256) void summary_kernel(const T* __restrict__ x0, 
   }
 #pragma unroll
   for (int it = 0; it < MAXIT; ++it) stage16[threadIdx.x + it * 256] = piece[it];
+  // SICS (SPADE 3.2, Eq. 4 rewritten as Eq. 5): ||sum of the unit-normalized
+  // tokens||^2, from registers.  Slot it of this thread holds piece
+  // tid % PIECES (CPL channels) of token (tid + 256*it) / PIECES, so the
+  // PIECES consecutive lanes that hold one token reduce its squared norm
+  // with a butterfly (a zero token gets weight 0 and adds nothing), and
+  // each lane adds its channels times that weight into w.  Slots past the
+  // block's end (re-read pieces) are skipped.  The lanes of the four waves
+  // that hold the same piece index are combined through the staging area
+  // once the channel walk below is done with it, so the workgroup needs no
+  // LDS beyond the 128-token stage.
+  constexpr int CPL = 16 / (int)sizeof(T);
+  float w[SICS ? CPL : 1];
+  if constexpr (SICS) {
+    static_assert(64 % PIECES == 0, "a token's pieces must sit in one wave");
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) w[e] = 0.0f;
+#pragma unroll
+    for (int it = 0; it < MAXIT; ++it) {
+      float v[CPL];
+      const uint32_t w4[4] = {piece[it].x, piece[it].y, piece[it].z, piece[it].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (sizeof(T) == 2) {
+          v[2 * e] = bf16_lo(w4[e]);
+          v[2 * e + 1] = bf16_hi(w4[e]);
+        } else {
+          v[e] = __uint_as_float(w4[e]);
+        }
+      }
+      float sq = 0.0f;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) sq = __builtin_fmaf(v[e], v[e], sq);
+#pragma unroll
+      for (int m = 1; m < PIECES; m <<= 1) sq += __shfl_xor(sq, m, 64);
+      const int u = ((int)threadIdx.x + it * 256) / PIECES;
+      const float inv = (u < n && sq > 0.0f) ? __builtin_amdgcn_rsqf(sq) : 0.0f;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) w[e] = __builtin_fmaf(v[e], inv, w[e]);
+    }
+#pragma unroll
+    for (int m = PIECES; m < 64; m <<= 1)
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) w[e] += __shfl_xor(w[e], m, 64);
+  }
   __syncthreads();
   const int c = threadIdx.x;
-  if (c >= D) return;
-  auto val = [&](int u) {
+  auto val = [&](int u, int ch) {
     if constexpr (sizeof(T) == 2)
-      return bf16_to_f32(stage[u * D + c]);
+      return bf16_to_f32(stage[u * D + ch]);
     else
-      return stage[u * D + c];
+      return stage[u * D + ch];
   };
-  float ra, rb = 0.0f;
-  if constexpr (!EXT) {
-    float acc = 0.0f;
-    for (int u = 0; u < n; ++u) acc = __fadd_rn(acc, val(u));
-    ra = __fdiv_rn(acc, (float)n);
-  } else {
-    float mx = -INFINITY, mn = INFINITY;
-    for (int u = 0; u < n; ++u) {
-      const float v = val(u);
-      mx = fmaxf(mx, v);
-      mn = fminf(mn, v);
+  if (c < D) {
+    float ra = 0.0f, rb = 0.0f;
+    if constexpr (!EXT) {
+      float acc = 0.0f;
+      for (int u = 0; u < n; ++u) acc = __fadd_rn(acc, val(u, c));
+      ra = __fdiv_rn(acc, (float)n);
+    } else {
+      float mx = -INFINITY, mn = INFINITY;
+      for (int u = 0; u < n; ++u) {
+        const float v = val(u, c);
+        mx = fmaxf(mx, v);
+        mn = fminf(mn, v);
+      }
+      ra = mid ? __fmul_rn(__fadd_rn(mx, mn), 0.5f) : mx;
+      rb = mn;
     }
-    ra = mid ? __fmul_rn(__fadd_rn(mx, mn), 0.5f) : mx;
-    rb = mn;
+    const size_t o = (second && cm1) ? ((size_t)bh * D + c) * g.NB + j : (size_t)item * D + c;
+    oa[o] = ra;
+    if (EXT && !mid) ob[o] = rb;
   }
-  const size_t o = (second && cm1) ? ((size_t)bh * D + c) * g.NB + j : (size_t)item * D + c;
-  oa[o] = ra;
-  if (EXT && !mid) ob[o] = rb;
+  if constexpr (SICS) {
+    float* part = reinterpret_cast<float*>(stage16);   // [4 waves][D] after the walk
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    __syncthreads();                                    // every walk read of the stage is done
+    if (lane < PIECES) {
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) part[wv * D + lane * CPL + e] = w[e];
+    }
+    __syncthreads();
+    float p2 = 0.0f;
+    if (c < D) {
+      const float wc = part[c] + part[D + c] + part[2 * D + c] + part[3 * D + c];
+      p2 = __builtin_fmaf(wc, wc, 0.0f);
+    }
+#pragma unroll
+    for (int m = 32; m > 0; m >>= 1) p2 += __shfl_xor(p2, m, 64);
+    __syncthreads();                                    // part[] reads done before it is reused
+    if (lane == 0) part[wv] = p2;
+    __syncthreads();
+    if (threadIdx.x == 0) (second ? sc1 : sc0)[item] = part[0] + part[1] + part[2] + part[3];
+  }
+}
+
+// dst row bh (per floats) = src row tensor_bh(bh), in 16-byte pieces.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                                          int per, HeadMap hm) {
+  const int bh = blockIdx.y;
+  const float4* s4 = reinterpret_cast<const float4*>(src + (size_t)hm.tensor_bh(bh) * per);
+  float4* d4 = reinterpret_cast<float4*>(dst + (size_t)bh * per);
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < per / 4; i += gridDim.x * 256) d4[i] = s4[i];
 }
 
 // Scores of RG query blocks against one key block for an estimator (EST 0:
@@ -552,40 +639,57 @@ __global__ __launch_bounds__(256) void scores_kernel(Summaries sm, float* __rest
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <bool EXT>
+template <bool EXT, bool SICS>
 hipError_t launch_summary(const void* x0, float* a0, float* b0, int mid0, const void* x1, float* a1, float* b1,
-                          int mid1, int dtype, int D, const DGeo& g, int BH, hipStream_t st, int cm1) {
+                          int mid1, int dtype, int D, const DGeo& g, int BH, hipStream_t st, int cm1,
+                          float* s0, float* s1, const HeadMap& hm) {
   dim3 grid((unsigned)(BH * g.NB), x1 ? 2 : 1), block(256);
   const size_t lds = (size_t)VSA_MAX_BLOCK_TOKENS * D * (dtype == 0 ? 2 : 4);   // every slot the copy writes
   if (dtype == 0) {
     if (D == 128)
-      hipLaunchKernelGGL((summary_kernel<uint16_t, 128, EXT>), grid, block, lds, st, (const uint16_t*)x0, a0, b0,
-                         mid0, (const uint16_t*)x1, a1, b1, mid1, g, cm1);
+      hipLaunchKernelGGL((summary_kernel<uint16_t, 128, EXT, SICS>), grid, block, lds, st, (const uint16_t*)x0, a0,
+                         b0, mid0, (const uint16_t*)x1, a1, b1, mid1, g, cm1, s0, s1, hm);
     else
-      hipLaunchKernelGGL((summary_kernel<uint16_t, 64, EXT>), grid, block, lds, st, (const uint16_t*)x0, a0, b0,
-                         mid0, (const uint16_t*)x1, a1, b1, mid1, g, cm1);
+      hipLaunchKernelGGL((summary_kernel<uint16_t, 64, EXT, SICS>), grid, block, lds, st, (const uint16_t*)x0, a0,
+                         b0, mid0, (const uint16_t*)x1, a1, b1, mid1, g, cm1, s0, s1, hm);
   } else {
     if (D == 128)
-      hipLaunchKernelGGL((summary_kernel<float, 128, EXT>), grid, block, lds, st, (const float*)x0, a0, b0, mid0,
-                         (const float*)x1, a1, b1, mid1, g, cm1);
+      hipLaunchKernelGGL((summary_kernel<float, 128, EXT, SICS>), grid, block, lds, st, (const float*)x0, a0, b0,
+                         mid0, (const float*)x1, a1, b1, mid1, g, cm1, s0, s1, hm);
     else
-      hipLaunchKernelGGL((summary_kernel<float, 64, EXT>), grid, block, lds, st, (const float*)x0, a0, b0, mid0,
-                         (const float*)x1, a1, b1, mid1, g, cm1);
+      hipLaunchKernelGGL((summary_kernel<float, 64, EXT, SICS>), grid, block, lds, st, (const float*)x0, a0, b0,
+                         mid0, (const float*)x1, a1, b1, mid1, g, cm1, s0, s1, hm);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_pool(const void* x0, float* out0, const void* x1, float* out1, int dtype, int D,
-                       const DGeo& g, int BH, hipStream_t st, bool out1_channel_major) {
-  return launch_summary<false>(x0, out0, nullptr, 0, x1, out1, nullptr, 0, dtype, D, g, BH, st,
-                               out1_channel_major ? 1 : 0);
+                       const DGeo& g, int BH, hipStream_t st, bool out1_channel_major, const HeadMap* hm) {
+  const HeadMap id;
+  return launch_summary<false, false>(x0, out0, nullptr, 0, x1, out1, nullptr, 0, dtype, D, g, BH, st,
+                                      out1_channel_major ? 1 : 0, nullptr, nullptr, hm ? *hm : id);
+}
+
+hipError_t launch_pool_sics(const void* x0, float* out0, const void* x1, float* out1, float* sics0, float* sics1,
+                            int dtype, int D, const DGeo& g, int BH, hipStream_t st) {
+  const HeadMap id;
+  return launch_summary<false, true>(x0, out0, nullptr, 0, x1, out1, nullptr, 0, dtype, D, g, BH, st, 1, sics0,
+                                     sics1, id);
 }
 
 hipError_t launch_extremes(const void* x0, float* max0, float* min0, int mid0, const void* x1, float* max1,
                            float* min1, int mid1, int dtype, int D, const DGeo& g, int BH, hipStream_t st,
-                           bool out1_channel_major) {
-  return launch_summary<true>(x0, max0, min0, mid0, x1, max1, min1, mid1, dtype, D, g, BH, st,
-                              out1_channel_major && !mid1 ? 1 : 0);
+                           bool out1_channel_major, const HeadMap* hm) {
+  const HeadMap id;
+  return launch_summary<true, false>(x0, max0, min0, mid0, x1, max1, min1, mid1, dtype, D, g, BH, st,
+                                     out1_channel_major && !mid1 ? 1 : 0, nullptr, nullptr, hm ? *hm : id);
+}
+
+hipError_t launch_gather_rows(const float* src, float* dst, int per, const HeadMap& hm, int BH, hipStream_t st) {
+  const int blocks = min(64, (per / 4 + 255) / 256);
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)max(blocks, 1), (unsigned)BH), dim3(256), 0, st, src, dst,
+                     per, hm);
+  return hipGetLastError();
 }
 
 // LDS of a workgroup with RT rows: RT rows of NB uint32 keys.

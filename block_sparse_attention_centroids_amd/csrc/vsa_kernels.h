@@ -36,6 +36,21 @@ struct SchemeArgs {
   int64_t off[VSA_MAX_SCHEMES];
 };
 
+// Heads a launch covers.  Row bh = b*n + s of the launch reads and writes
+// tensor head b*total + h[s] of tensors that hold `total` heads; identity
+// when a launch covers every head in order (n == total, h unused).
+struct HeadMap {
+  int32_t n = 1;
+  int32_t total = 1;
+  int32_t identity = 1;
+  int16_t h[VSA_MAX_HEADS] = {};
+  __device__ __host__ int tensor_bh(int bh) const {
+    if (identity) return bh;
+    const int b = bh / n;
+    return b * total + h[bh - b * n];
+  }
+};
+
 // Block summaries an estimator reads, each float32 [BH][NB][D]: mean: qa =
 // query means, ka = key means; DSA: qa = query midpoints, ka/kb = key
 // max/min; DSA2: qa/qb = query max/min, ka/kb = key max/min.  With kt set
@@ -53,12 +68,21 @@ struct Summaries {
 // Block means of x0 into out0 and, when x1 is not null, of x1 into out1
 // ([BH][NB][D], or [BH][D][NB] for out1 when out1_channel_major).
 hipError_t launch_pool(const void* x0, float* out0, const void* x1, float* out1, int dtype, int D,
-                       const DGeo& g, int BH, hipStream_t st, bool out1_channel_major = false);
+                       const DGeo& g, int BH, hipStream_t st, bool out1_channel_major = false,
+                       const HeadMap* hm = nullptr);
+// Block means as launch_pool (x1's channel-major) and, in the same pass,
+// every block's SICS (sum of the pairwise cosine similarities of its
+// tokens) of x0 into sics0 and of x1 into sics1 ([BH][NB]).
+hipError_t launch_pool_sics(const void* x0, float* out0, const void* x1, float* out1, float* sics0, float* sics1,
+                            int dtype, int D, const DGeo& g, int BH, hipStream_t st);
+// dst[bh][0 .. per) = src[tensor_bh(bh)][0 .. per) for the BH rows of a
+// launch (per a multiple of 4 floats).
+hipError_t launch_gather_rows(const float* src, float* dst, int per, const HeadMap& hm, int BH, hipStream_t st);
 // Block max/min of x0 (or, with mid0, the midpoint into max0) and of x1
 // (channel-major when out1_channel_major and not mid1).
 hipError_t launch_extremes(const void* x0, float* max0, float* min0, int mid0, const void* x1, float* max1,
                            float* min1, int mid1, int dtype, int D, const DGeo& g, int BH, hipStream_t st,
-                           bool out1_channel_major = false);
+                           bool out1_channel_major = false, const HeadMap* hm = nullptr);
 // est: 0 mean, 1 DSA, 2 DSA2 (vsa_estimator).
 hipError_t launch_score_select(const Summaries& sm, int est, const DGeo& g, int D, int heads, int BH,
                                const SelectArgs& sa, int32_t* row_ptr, int32_t* col_idx, int32_t* counts,
@@ -71,7 +95,7 @@ hipError_t launch_scores(const Summaries& sm, int est, float* out, int NB, int D
 // work); otherwise an equal contiguous slice of every head.
 hipError_t launch_attn(const void* q, const void* k, const void* v, void* o, int dtype, int D,
                        const int32_t* row_ptr, const int32_t* col_idx, const DGeo& g, int BH,
-                       float scale, bool contiguous, hipStream_t st);
+                       float scale, bool contiguous, hipStream_t st, const HeadMap* hm = nullptr);
 // Per-block SICS of x0 into out0 and, when x1 is not null, of x1 into out1.
 hipError_t launch_sics(const void* x0, float* out0, const void* x1, float* out1, int dtype, int D,
                        const DGeo& g, int BH, hipStream_t st);

@@ -331,6 +331,55 @@ vsa_status vsa_select_scheme(const void* q, const void* k, const vsa_shape* shap
 vsa_status vsa_plan_noalloc(const void* q, const void* k, const vsa_shape* shape, const float* density,
                             int n_density, int window_t, vsa_index* index, void* stream);
 
+/* Calls over a subset of the heads (SPADE 3.2 selects a blocking scheme
+ * per head, and 3.3 groups the heads that share one into a launch): q, k,
+ * v and o hold shape->heads heads ("total": [B, total, N, D]); the call
+ * covers the n_heads heads listed in `heads` (host int32, distinct, each in
+ * [0, total); 1 <= n_heads <= total, n_heads <= VSA_MAX_HEADS, total <=
+ * 32767), all under shape's blocking.  Index row r = (b*n_heads + s)*NB + i
+ * belongs to head heads[s]; index->shape is shape with heads = n_heads, so
+ * vsa_query on that shape gives the index sizes and the workspace, and
+ * density has 1 or n_heads entries (one per listed head).
+ * qmeans, kmeans: NULL to summarize the listed heads of q and k, or the
+ *   block means of every head under shape's blocking as
+ *   vsa_select_scheme_means leaves them (query means [B*total][NB][D], key
+ *   means [B*total][D][NB]); then q and k are not read (may be NULL) and
+ *   the plan is the one vsa_plan computes, bit for bit.
+ * Bad head lists are VSA_ERR_INVALID_ARG (VSA_ERR_UNSUPPORTED past the
+ * limits).  Other arguments and errors as in vsa_plan. */
+vsa_status vsa_plan_heads(const void* q, const void* k, const float* qmeans, const float* kmeans,
+                          const vsa_shape* shape, const int32_t* heads, int n_heads, const float* density,
+                          int n_density, int window_t, vsa_index* index, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* vsa_attn for an index from vsa_plan_heads: heads (host int32) lists the
+ * index->shape.heads heads it covers, in its row order, among the
+ * heads_total heads of q, k, v and o; only those heads of o are written.
+ * Other arguments and errors as in vsa_attn. */
+vsa_status vsa_attn_heads(const void* q, const void* k, const void* v, const vsa_index* index,
+                          const int32_t* heads, int heads_total, float scale, void* o, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* Workspace of vsa_select_scheme_means (host only): ws_bytes, and, when
+ * means_off (host [2*n_cand]) is not NULL, the byte offsets in it of each
+ * candidate c's query means (means_off[2c], float32 [B*heads][NB_c][D]) and
+ * key means (means_off[2c+1], float32 [B*heads][D][NB_c]).  Candidates as
+ * in vsa_scheme_workspace. */
+vsa_status vsa_scheme_means_workspace(const vsa_shape* shape, const int32_t* candidates, int n_cand,
+                                      size_t* ws_bytes, size_t* means_off);
+
+/* vsa_select_scheme (same scores and choice, up to float32 rounding of the
+ * SICS sums) that, in the same pass over Q and K per candidate, also leaves
+ * every candidate's block means of Q and K in ws at the offsets
+ * vsa_scheme_means_workspace reports, in the planner's float32 order.  A
+ * head's plan at its chosen candidate can then start from them
+ * (vsa_plan_heads with qmeans/kmeans) without reading Q and K again:
+ * SPADE 3.3 fuses blocking, summarization and intra-block estimation into
+ * one pass. */
+vsa_status vsa_select_scheme_means(const void* q, const void* k, const vsa_shape* shape,
+                                   const int32_t* candidates, int n_cand, float* scores, int32_t* choice,
+                                   void* ws, size_t ws_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* vsa_status_str(vsa_status s);
 

@@ -448,3 +448,76 @@ def test_attn_out_argument_is_checked_before_any_launch():
         _check_out(q, torch.empty((2, 1, 256, 64), dtype=torch.bfloat16))      # same numel, other shape
     with pytest.raises(TypeError):
         _check_out(q, None)
+
+
+def _heads(*hs):
+    return (ctypes.c_int32 * len(hs))(*hs)
+
+
+def test_head_subset_entry_error_paths(lib):
+    """vsa_plan_heads / vsa_attn_heads reject bad head lists and pointers
+    with the documented status before anything is enqueued (fake device
+    pointers are never touched)."""
+    w = W.WORKLOADS["wan13b"]
+    shape = _shape(w)
+    dens = (ctypes.c_float * 1)(0.2)
+    sub = VsaShape(w.B, 3, w.D, *w.grid, *w.block, _lib.VSA_BF16)
+    st, rl, cap, pws, _ = _query(lib, sub, [0.2])
+    assert st == 0
+
+    def plan(hl, n, q=FAKE, qm=None, km=None, cap_=cap, ws=FAKE, wsb=pws, dens_=dens, nd=1, win=-1):
+        idx = VsaIndex(sub, 0, 0, FAKE, FAKE, cap_)
+        return lib.vsa_plan_heads(q, q, qm, km, ctypes.byref(shape), hl, n, dens_, nd, win, ctypes.byref(idx), ws,
+                                  wsb, None)
+
+    assert plan(_heads(0, 5, 11), 0) == _lib.VSA_ERR_INVALID_ARG           # no heads
+    assert plan(None, 3) == _lib.VSA_ERR_INVALID_ARG                       # no list
+    assert plan(_heads(0, 5, 5), 3) == _lib.VSA_ERR_INVALID_ARG            # repeated head
+    assert plan(_heads(0, 5, 12), 3) == _lib.VSA_ERR_INVALID_ARG           # past the tensor's heads
+    assert plan(_heads(0, -1, 2), 3) == _lib.VSA_ERR_INVALID_ARG
+    assert plan(_heads(*range(13)), 13) == _lib.VSA_ERR_INVALID_ARG        # more heads than the tensors hold
+    assert plan(_heads(0, 5, 11), 3, q=None) == _lib.VSA_ERR_INVALID_ARG   # neither q/k nor means
+    assert plan(_heads(0, 5, 11), 3, q=None, qm=FAKE) == _lib.VSA_ERR_INVALID_ARG   # one of the two means
+    assert plan(_heads(0, 5, 11), 3, cap_=cap - 1) == _lib.VSA_ERR_CAPACITY
+    assert plan(_heads(0, 5, 11), 3, wsb=pws - 1) == _lib.VSA_ERR_WORKSPACE
+    three = (ctypes.c_float * 3)(0.2, 0.1, 0.3)
+    # per-head densities pass every check before the workspace size
+    assert plan(_heads(0, 5, 11), 3, dens_=three, nd=3, cap_=1 << 30, wsb=pws - 1) == _lib.VSA_ERR_WORKSPACE
+    assert plan(_heads(0, 5, 11), 3, dens_=three, nd=2) == _lib.VSA_ERR_INVALID_ARG
+    assert plan(_heads(0, 5, 11), 3, win=-2) == _lib.VSA_ERR_INVALID_ARG
+
+    idx = VsaIndex(sub, 336, -1, FAKE, FAKE, cap)
+    attn = lambda hl, total, index=idx: lib.vsa_attn_heads(FAKE, FAKE, FAKE, ctypes.byref(index), hl, total, 0.0,
+                                                           FAKE, None, 0, None)
+    assert attn(_heads(0, 5, 5), 12) == _lib.VSA_ERR_INVALID_ARG
+    assert attn(_heads(0, 5, 12), 12) == _lib.VSA_ERR_INVALID_ARG
+    assert attn(_heads(0, 5, 11), 2) == _lib.VSA_ERR_INVALID_ARG           # fewer tensor heads than listed
+    bad = VsaIndex(sub, 335, -1, FAKE, FAKE, cap)
+    assert attn(_heads(0, 5, 11), 12, bad) == _lib.VSA_ERR_SHAPE_MISMATCH
+    assert lib.vsa_attn_heads(FAKE, FAKE, None, ctypes.byref(idx), _heads(0, 5, 11), 12, 0.0, FAKE, None, 0,
+                              None) == _lib.VSA_ERR_INVALID_ARG
+
+
+def test_scheme_means_workspace_layout(lib):
+    """The means regions follow the SICS regions, one query and one key
+    region per candidate, each B*heads*NB_c*D floats, 256-byte aligned."""
+    w = W.WORKLOADS["wan13b"]
+    shape = _shape(w)
+    cands = [(4, 4, 8), (1, 8, 16), (2, 8, 8)]
+    flat = (ctypes.c_int32 * 9)(*[a for c in cands for a in c])
+    base, total = ctypes.c_size_t(), ctypes.c_size_t()
+    offs = (ctypes.c_size_t * 6)()
+    assert lib.vsa_scheme_workspace(ctypes.byref(shape), flat, 3, ctypes.byref(base)) == 0
+    assert lib.vsa_scheme_means_workspace(ctypes.byref(shape), flat, 3, ctypes.byref(total), offs) == 0
+    prev_end = base.value
+    for c, blk in enumerate(cands):
+        nb = O.geometry(w.grid, blk).NB
+        one = w.B * w.heads * nb * w.D * 4
+        assert offs[2 * c] >= prev_end and offs[2 * c] % 256 == 0 and offs[2 * c + 1] % 256 == 0
+        assert offs[2 * c + 1] >= offs[2 * c] + one
+        prev_end = offs[2 * c + 1] + one
+    assert total.value >= prev_end
+    assert lib.vsa_scheme_means_workspace(ctypes.byref(shape), flat, 0, ctypes.byref(total), None) == \
+        _lib.VSA_ERR_INVALID_ARG
+    assert lib.vsa_select_scheme_means(FAKE, FAKE, ctypes.byref(shape), flat, 3, FAKE, FAKE, FAKE,
+                                       total.value - 1, None) == _lib.VSA_ERR_WORKSPACE
