@@ -341,17 +341,49 @@ def time_cold(attn_call, stream, reps=10, scratch_mib=512):
     return float(np.median(ms))
 
 
+def mfma_sustained(vsa, stream, seconds=3.0, n_wg=4096, iters=2000):
+    """Sustained bf16 MFMA rate of this card on N(0,1) operands held in
+    registers (vsa_calib_mfma_bf16): the practical matrix-core ceiling
+    under the card's power limit, timed with HIP events on `stream` until
+    `seconds` of launches have run; the median rate over the second half
+    of the launches (after the clock has settled) is reported."""
+    import torch
+    from block_sparse_attention_centroids_amd import _lib
+    g = torch.Generator().manual_seed(0)
+    pool = torch.randn(_lib.VSA_CALIB_POOL_BYTES // 2, generator=g).to(torch.bfloat16).view(torch.uint8).to("cuda")
+    out = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda")
+    flop = n_wg * 4 * iters * 16 * 32768
+    vsa.calib_mfma_bf16(pool, out, n_wg, 10)
+    torch.cuda.synchronize()
+    ms, t0 = [], time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        vsa.calib_mfma_bf16(pool, out, n_wg, iters)
+        e1.record(stream)
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    half = np.array(ms[len(ms) // 2:])
+    med = float(np.median(half))
+    return {"tflops": round(flop / (med * 1e-3) / 1e12, 1), "launch_ms_median": round(med, 3),
+            "launches": len(ms), "seconds": round(time.perf_counter() - t0, 2),
+            "data": "N(0,1) bf16 operands in registers, 32x32x16 MFMAs only",
+            "kernel": f"vsa_calib_mfma_bf16 ({n_wg} workgroups x 4 waves x {iters} x 16 MFMAs)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="wan13b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the scheme-selection, selection-variant and mixed-plan timings "
                          "(profiled runs: only the step's own launches)")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--calib-seconds", type=float, default=3.0,
+                    help="seconds of the sustained-MFMA measurement after the timed steps (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run one plain device-to-device copy of MIB MiB (HBM counter scale)")
     a = ap.parse_args()
@@ -519,6 +551,11 @@ def main():
         result["attn_cold"] = {"scratch_MiB_between_calls": 512, "attn_ms_median": round(cold, 4),
                                "attn_tflops": round(flops / (cold * 1e-3) / 1e12, 2),
                                "warm_attn_ms": result["attn_ms"]}
+    if a.calib_seconds > 0 and w.dtype == "bf16":
+        print("[bench] sustained MFMA rate", file=sys.stderr, flush=True)
+        ms_ = mfma_sustained(vsa, stream, a.calib_seconds)
+        ms_["attn_frac_of_sustained"] = round(attn_tflops / ms_["tflops"], 4)
+        result["mfma_sustained"] = ms_
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(inp, w, rp, ci, sizes, flops, a.cpu_budget)

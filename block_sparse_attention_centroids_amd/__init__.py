@@ -25,7 +25,7 @@ from ._lib import VsaError, VsaHeadOption, VsaIndex, VsaSelect, VsaShape, check,
 
 __all__ = ["plan", "plan_noalloc", "plan_heads", "attn_heads", "select_scheme_means", "plan_schemes",
            "attn_schemes", "SchemeMeans", "SchemePlan", "plan_select", "plan_mixed", "attn", "query", "query_select", "permute", "unpermute",
-           "centroids", "centroid_scores", "estimate", "sics", "select_scheme", "Index", "VsaError", "load"]
+           "centroids", "centroid_scores", "estimate", "sics", "select_scheme", "calib_mfma_bf16", "Index", "VsaError", "load"]
 
 _DTYPES = {torch.bfloat16: _lib.VSA_BF16, torch.float32: _lib.VSA_F32}
 
@@ -561,3 +561,19 @@ def attn_schemes(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sp: SchemePl
     for _, _, hs, idx in sp.groups:
         attn_heads(q, k, v, idx, hs, out=o)
     return o
+
+
+def calib_mfma_bf16(pool: torch.Tensor, out: torch.Tensor, n_workgroups: int, iters: int) -> None:
+    """Launch the sustained bf16 MFMA-rate kernel (a measurement aid, not a
+    step of the method) on the current stream: pool is a device uint8
+    tensor of at least VSA_CALIB_POOL_BYTES bytes of bf16 operands, out a
+    device float32 tensor of n_workgroups * 256 entries.  Work per launch:
+    n_workgroups * 4 * iters * 16 * 32768 FLOP."""
+    lib = load()
+    if pool.device.type != "cuda" or out.device.type != "cuda" or out.dtype != torch.float32:
+        raise ValueError("pool and out must be device tensors, out float32")
+    if not pool.is_contiguous() or not out.is_contiguous() or out.numel() < n_workgroups * 256:
+        raise ValueError("out must be contiguous with n_workgroups * 256 entries")
+    check(lib.vsa_calib_mfma_bf16(ctypes.c_void_p(pool.data_ptr()), pool.numel() * pool.element_size(),
+                                  ctypes.c_void_p(out.data_ptr()), int(n_workgroups), int(iters),
+                                  _stream(out)), "vsa_calib_mfma_bf16")

@@ -30,6 +30,9 @@ VSA_HEAD_STATIC = 1
 VSA_HEAD_DENSE = 2
 
 VSA_PLAN_NOALLOC_MAX_WS = 32 << 20
+VSA_CALIB_POOL_BYTES = 4 << 20
+VSA_CALIB_MAX_WORKGROUPS = 65536
+VSA_CALIB_MAX_ITERS = 100000
 
 
 class VsaShape(ctypes.Structure):
@@ -67,7 +70,7 @@ EXPORTS = ("vsa_query", "vsa_plan", "vsa_attn", "vsa_permute", "vsa_unpermute",
            "vsa_centroids", "vsa_centroid_scores", "vsa_sics", "vsa_scheme_workspace",
            "vsa_select_scheme", "vsa_query_select", "vsa_plan_select", "vsa_estimate", "vsa_query_mixed", "vsa_plan_mixed",
            "vsa_plan_noalloc", "vsa_plan_heads", "vsa_attn_heads", "vsa_scheme_means_workspace",
-           "vsa_select_scheme_means", "vsa_status_str")
+           "vsa_select_scheme_means", "vsa_calib_mfma_bf16", "vsa_status_str")
 
 
 def load() -> ctypes.CDLL:
@@ -120,6 +123,7 @@ def load() -> ctypes.CDLL:
                                                ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
     lib.vsa_select_scheme_means.argtypes = [P, P, ctypes.POINTER(VsaShape), ctypes.POINTER(ctypes.c_int32), I, P,
                                             P, P, ctypes.c_size_t, P]
+    lib.vsa_calib_mfma_bf16.argtypes = [P, ctypes.c_size_t, P, I, I, P]
     for name in EXPORTS[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     lib.vsa_status_str.argtypes = [ctypes.c_int]

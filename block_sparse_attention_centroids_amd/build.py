@@ -34,6 +34,7 @@ SOURCES = {
     "layout.hip": [],
     "schemes.hip": [],
     "api.hip": [],
+    "calib.hip": [],
 }
 
 

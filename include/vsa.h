@@ -380,6 +380,33 @@ vsa_status vsa_select_scheme_means(const void* q, const void* k, const vsa_shape
                                    const int32_t* candidates, int n_cand, float* scores, int32_t* choice,
                                    void* ws, size_t ws_bytes, void* stream);
 
+/* Measurement aid, not a step of the method: the bf16 matrix-core rate
+ * this GPU sustains, the ceiling against which the attention kernel's rate
+ * can be read beside the published dense peak (which assumes the full
+ * 2.4 GHz clock; under load the clock depends on power, and power on the
+ * data the matrix cores switch).  n_workgroups workgroups of 4 waves each
+ * run `iters` rounds of 16 v_mfma_f32_32x32x16_bf16 on register operands
+ * loaded once from pool; nothing else runs in the loop.  Work per call:
+ * n_workgroups * 4 * iters * 16 * 32768 FLOP.
+ * pool: device, at least VSA_CALIB_POOL_BYTES bytes, 16-byte aligned: 4096
+ *   fragments of 64 lanes x 8 bf16, lane l of fragment f at byte
+ *   (f*64 + l)*16.  Wave w of workgroup g uses fragments
+ *   (16*(4g + w) + j) mod 4096 for j = 0..15, 0-7 as A operands and 8-15 as
+ *   B operands (A lane l holds row l mod 32, B lane l column l mod 32, both
+ *   with inner indices 8*(l/32) .. 8*(l/32)+7).  Round r multiplies
+ *   A_j x B_(j+3 mod 8) and A_(j+5 mod 8) x B_j for j = 0..7.
+ * out: device float32 [n_workgroups * 256]: thread t of workgroup g writes
+ *   the sum of its accumulator elements at g*256 + t, so a wave's 64 values
+ *   add up to the sum of every entry of its products.
+ * Limits: 1 <= n_workgroups <= VSA_CALIB_MAX_WORKGROUPS, 1 <= iters <=
+ * VSA_CALIB_MAX_ITERS, else VSA_ERR_INVALID_ARG (also for NULL or
+ * misaligned pointers); a failed launch is VSA_ERR_HIP.  Allocates nothing. */
+#define VSA_CALIB_POOL_BYTES ((size_t)4 << 20)
+#define VSA_CALIB_MAX_WORKGROUPS 65536
+#define VSA_CALIB_MAX_ITERS 100000
+vsa_status vsa_calib_mfma_bf16(const void* pool, size_t pool_bytes, float* out, int n_workgroups, int iters,
+                               void* stream);
+
 /* Static description of a status code. */
 const char* vsa_status_str(vsa_status s);
 

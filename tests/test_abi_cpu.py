@@ -521,3 +521,23 @@ def test_scheme_means_workspace_layout(lib):
         _lib.VSA_ERR_INVALID_ARG
     assert lib.vsa_select_scheme_means(FAKE, FAKE, ctypes.byref(shape), flat, 3, FAKE, FAKE, FAKE,
                                        total.value - 1, None) == _lib.VSA_ERR_WORKSPACE
+
+
+def test_calib_entry_error_paths(lib):
+    """Every case fails one of the argument checks, which all come before
+    the launch, so no fake pointer is ever handed to a kernel."""
+    P = _lib.VSA_CALIB_POOL_BYTES
+
+    def call(pool=FAKE, nbytes=P, out=FAKE, nwg=8, iters=1):
+        return lib.vsa_calib_mfma_bf16(pool, nbytes, out, nwg, iters, None)
+
+    bad = _lib.VSA_ERR_INVALID_ARG
+    assert call(pool=None) == bad
+    assert call(out=None) == bad
+    assert call(pool=ctypes.c_void_p(0x100008)) == bad          # pool not 16-byte aligned
+    assert call(out=ctypes.c_void_p(0x100002)) == bad           # out not 4-byte aligned
+    assert call(nbytes=P - 1) == bad
+    assert call(nwg=0) == bad and call(nwg=-3) == bad
+    assert call(nwg=_lib.VSA_CALIB_MAX_WORKGROUPS + 1) == bad
+    assert call(iters=0) == bad
+    assert call(iters=_lib.VSA_CALIB_MAX_ITERS + 1) == bad
