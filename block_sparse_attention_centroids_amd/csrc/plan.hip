@@ -24,9 +24,10 @@ namespace vsa {
 // ---------------------------------------------------------------------------
 // Block summaries (means for the mean estimator, max/min or the midpoint for
 // the box estimators).  One workgroup per (tensor, row bh, block j).  The
-// workgroup copies the block's n tokens into LDS in 16-byte pieces (every
-// load coalesced, as in the layout kernels); then thread c walks channel c
-// over the tokens in block order.  The mean adds them one by one from +0
+// workgroup loads the block's n tokens in 16-byte pieces (every load
+// coalesced, as in the layout kernels) and stages them through LDS half a
+// block (64 tokens) at a time; thread c walks channel c over the tokens in
+// block order.  The mean adds them one by one from +0
 // and divides once (correctly rounded); max and min are exact.  The query
 // midpoint is fl(fl(max + min) * 0.5).  With cm1 the second tensor's
 // summaries go channel-major ([BH][D][NB]).
@@ -67,21 +68,31 @@ __global__ __launch_bounds__(256) void summary_kernel(const T* __restrict__ x0, 
   map.init(g, b);
   const uint8_t* src = reinterpret_cast<const uint8_t*>(x) + (size_t)hm.tensor_bh(bh) * g.N * ROWB;
   // Every piece a thread copies is loaded before any is stored, so the
-  // loads are all in flight together.  Loads and stores are unconditional,
-  // so no branch splits them: a slot past the block's last piece re-reads
-  // that piece into LDS sized for the largest block (128 tokens), where the
-  // channel walk below never reads it.
+  // loads are all in flight together.  Loads are unconditional, so no
+  // branch splits them: a slot past the block's last piece re-reads that
+  // piece, and the channel walk below never reads it.
   constexpr int MAXIT = (VSA_MAX_BLOCK_TOKENS * PIECES + 255) / 256;
   const int npieces = n * PIECES;
-  uint4 piece[MAXIT];
-#pragma unroll
-  for (int it = 0; it < MAXIT; ++it) {
+  // The LDS stage holds half a block (64 tokens): the first half's pieces
+  // (pa) go to LDS first, the second half's (pb) stay in registers until
+  // the walk over the first half is done.  16 KB of LDS per workgroup (bf16,
+  // d = 128) lets 8 workgroups share a CU, so twice as many loads are in
+  // flight per CU as with a whole-block stage.
+  constexpr int HALF_IT = MAXIT / 2;
+  constexpr int HALF_TOK = VSA_MAX_BLOCK_TOKENS / 2;
+  static_assert(256 * HALF_IT == HALF_TOK * PIECES, "half the slots hold the first 64 tokens");
+  uint4 pa[HALF_IT], pb[HALF_IT];
+  auto load_piece = [&](int it) {
     const int idx = min((int)threadIdx.x + it * 256, npieces - 1);
     const int u = idx / PIECES, p = idx - u * PIECES;
-    piece[it] = *reinterpret_cast<const uint4*>(src + (size_t)map(u) * ROWB + p * 16);
-  }
+    return *reinterpret_cast<const uint4*>(src + (size_t)map(u) * ROWB + p * 16);
+  };
 #pragma unroll
-  for (int it = 0; it < MAXIT; ++it) stage16[threadIdx.x + it * 256] = piece[it];
+  for (int it = 0; it < HALF_IT; ++it) pa[it] = load_piece(it);
+#pragma unroll
+  for (int it = 0; it < HALF_IT; ++it) pb[it] = load_piece(HALF_IT + it);
+#pragma unroll
+  for (int it = 0; it < HALF_IT; ++it) stage16[threadIdx.x + it * 256] = pa[it];
   // SICS (SPADE 3.2, Eq. 4 rewritten as Eq. 5): ||sum of the unit-normalized
   // tokens||^2, from registers.  Slot it of this thread holds piece
   // tid % PIECES (CPL channels) of token (tid + 256*it) / PIECES, so the
@@ -91,7 +102,7 @@ __global__ __launch_bounds__(256) void summary_kernel(const T* __restrict__ x0, 
   // block's end (re-read pieces) are skipped.  The lanes of the four waves
   // that hold the same piece index are combined through the staging area
   // once the channel walk below is done with it, so the workgroup needs no
-  // LDS beyond the 128-token stage.
+  // LDS beyond the 64-token stage.
   constexpr int CPL = 16 / (int)sizeof(T);
   float w[SICS ? CPL : 1];
   if constexpr (SICS) {
@@ -101,7 +112,8 @@ __global__ __launch_bounds__(256) void summary_kernel(const T* __restrict__ x0, 
 #pragma unroll
     for (int it = 0; it < MAXIT; ++it) {
       float v[CPL];
-      const uint32_t w4[4] = {piece[it].x, piece[it].y, piece[it].z, piece[it].w};
+      const uint4 pc = it < HALF_IT ? pa[it] : pb[it - HALF_IT];
+      const uint32_t w4[4] = {pc.x, pc.y, pc.z, pc.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if constexpr (sizeof(T) == 2) {
@@ -134,19 +146,41 @@ __global__ __launch_bounds__(256) void summary_kernel(const T* __restrict__ x0, 
     else
       return stage[u * D + ch];
   };
+  float acc = 0.0f, mx = -INFINITY, mn = INFINITY;
+  const int n0 = min(n, HALF_TOK);
   if (c < D) {
-    float ra = 0.0f, rb = 0.0f;
     if constexpr (!EXT) {
-      float acc = 0.0f;
-      for (int u = 0; u < n; ++u) acc = __fadd_rn(acc, val(u, c));
-      ra = __fdiv_rn(acc, (float)n);
+      for (int u = 0; u < n0; ++u) acc = __fadd_rn(acc, val(u, c));
     } else {
-      float mx = -INFINITY, mn = INFINITY;
-      for (int u = 0; u < n; ++u) {
+      for (int u = 0; u < n0; ++u) {
         const float v = val(u, c);
         mx = fmaxf(mx, v);
         mn = fminf(mn, v);
       }
+    }
+  }
+  if (n > HALF_TOK) {                       // uniform over the workgroup
+    __syncthreads();                        // every read of the first half is done
+#pragma unroll
+    for (int it = 0; it < HALF_IT; ++it) stage16[threadIdx.x + it * 256] = pb[it];
+    __syncthreads();
+    if (c < D) {
+      if constexpr (!EXT) {
+        for (int u = 0; u < n - HALF_TOK; ++u) acc = __fadd_rn(acc, val(u, c));
+      } else {
+        for (int u = 0; u < n - HALF_TOK; ++u) {
+          const float v = val(u, c);
+          mx = fmaxf(mx, v);
+          mn = fminf(mn, v);
+        }
+      }
+    }
+  }
+  if (c < D) {
+    float ra, rb = 0.0f;
+    if constexpr (!EXT) {
+      ra = __fdiv_rn(acc, (float)n);
+    } else {
       ra = mid ? __fmul_rn(__fadd_rn(mx, mn), 0.5f) : mx;
       rb = mn;
     }
@@ -644,7 +678,7 @@ hipError_t launch_summary(const void* x0, float* a0, float* b0, int mid0, const 
                           int mid1, int dtype, int D, const DGeo& g, int BH, hipStream_t st, int cm1,
                           float* s0, float* s1, const HeadMap& hm) {
   dim3 grid((unsigned)(BH * g.NB), x1 ? 2 : 1), block(256);
-  const size_t lds = (size_t)VSA_MAX_BLOCK_TOKENS * D * (dtype == 0 ? 2 : 4);   // every slot the copy writes
+  const size_t lds = (size_t)(VSA_MAX_BLOCK_TOKENS / 2) * D * (dtype == 0 ? 2 : 4);   // half a block of tokens
   if (dtype == 0) {
     if (D == 128)
       hipLaunchKernelGGL((summary_kernel<uint16_t, 128, EXT, SICS>), grid, block, lds, st, (const uint16_t*)x0, a0,
