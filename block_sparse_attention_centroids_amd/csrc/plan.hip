@@ -308,8 +308,9 @@ __device__ inline uint32_t wave_max_u(uint32_t v) {
 // Top-K cut of a row of keys: thr = the k-th largest key, need = how many
 // keys equal to thr are kept (the lowest ids).  thr grows bit by bit from
 // the top to the largest value with at least kk keys >= thr; counts are
-// ballots, and rows of at most 512 blocks keep their keys in registers
-// (4, 6 or 8 chunks of 64, the fewest that hold the row).
+// ballots, and rows of at most 1280 blocks keep their keys in registers
+// (4, 6, 8, 12, 16 or 20 chunks of 64, the fewest that hold the row), so
+// the 32 passes read LDS once; longer rows re-read it every pass.
 template <int NR>
 __device__ inline uint32_t topk_threshold_regs(const uint32_t* keys, int NB, int lane, int kk, int& gt) {
   uint32_t kv[NR];
@@ -342,6 +343,12 @@ __device__ inline void topk_cut(const uint32_t* keys, int NB, int lane, int kk, 
     thr = topk_threshold_regs<6>(keys, NB, lane, kk, gt);
   } else if (NB <= 64 * 8) {
     thr = topk_threshold_regs<8>(keys, NB, lane, kk, gt);
+  } else if (NB <= 64 * 12) {
+    thr = topk_threshold_regs<12>(keys, NB, lane, kk, gt);
+  } else if (NB <= 64 * 16) {
+    thr = topk_threshold_regs<16>(keys, NB, lane, kk, gt);
+  } else if (NB <= 64 * 20) {
+    thr = topk_threshold_regs<20>(keys, NB, lane, kk, gt);
   } else {
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = thr | (1u << bit);
@@ -564,6 +571,12 @@ __global__ __launch_bounds__(256) void score_select_kernel(
         topp_cut_regs<6>(keys, NB, lane, sa.p[h], sa.scale, thr, need);
       else if (NB <= 64 * 8)
         topp_cut_regs<8>(keys, NB, lane, sa.p[h], sa.scale, thr, need);
+      else if (NB <= 64 * 12)
+        topp_cut_regs<12>(keys, NB, lane, sa.p[h], sa.scale, thr, need);
+      else if (NB <= 64 * 16)
+        topp_cut_regs<16>(keys, NB, lane, sa.p[h], sa.scale, thr, need);
+      else if (NB <= 64 * 20)
+        topp_cut_regs<20>(keys, NB, lane, sa.p[h], sa.scale, thr, need);
       else
         topp_cut_lds(keys, NB, lane, sa.p[h], sa.scale, thr, need);
     } else {

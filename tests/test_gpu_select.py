@@ -140,10 +140,12 @@ def test_small_select_parity(vsa, case):
     _say(f"[gpu]   ok rows={rows} band={band} nnz={idx.nnz()} max-abs {err.max():.2e}")
 
 
-# Rows of NB blocks keep their keys in 4, 6 or 8 register chunks of 64 (the
-# fewest that hold the row) and longer rows in LDS: each width at its edges.
+# Rows of NB blocks keep their keys in 4, 6, 8, 12, 16 or 20 register chunks
+# of 64 (the fewest that hold the row) and longer rows in LDS: each width at
+# its edges.
 WIDTHS = [(256, (1, 32, 32)), (257, (1, 2, 514)), (384, (1, 32, 48)), (385, (1, 10, 154)),
-          (512, (1, 32, 64)), (513, (1, 54, 38))]
+          (512, (1, 32, 64)), (513, (1, 54, 38)), (768, (1, 32, 96)), (769, (1, 2, 1538)),
+          (1024, (1, 64, 64)), (1025, (1, 50, 82)), (1280, (1, 64, 80)), (1281, (1, 42, 122))]
 
 
 @pytest.mark.parametrize("mode,val", [("topk", 0.3), ("topp", 0.5)])
