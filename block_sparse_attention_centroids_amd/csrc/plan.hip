@@ -299,6 +299,12 @@ __device__ inline float wave_sum_f(float a) {
   return uniform_f(a);
 }
 
+__device__ inline uint32_t wave_min_u(uint32_t v) {
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, m, 64));
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+
 __device__ inline uint32_t wave_max_u(uint32_t v) {
 #pragma unroll
   for (int m = 32; m > 0; m >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, m, 64));
@@ -310,7 +316,10 @@ __device__ inline uint32_t wave_max_u(uint32_t v) {
 // the top to the largest value with at least kk keys >= thr; counts are
 // ballots, and rows of at most 1280 blocks keep their keys in registers
 // (4, 6, 8, 12, 16 or 20 chunks of 64, the fewest that hold the row), so
-// the 32 passes read LDS once; longer rows re-read it every pass.
+// the 32 passes read LDS once; longer rows re-read it every pass.  Once
+// exactly kk keys are >= the candidate, those kk are the top kk and the
+// cut is their minimum, so the remaining passes are skipped (the result is
+// the same key the full search reaches).
 template <int NR>
 __device__ inline uint32_t topk_threshold_regs(const uint32_t* keys, int NB, int lane, int kk, int& gt) {
   uint32_t kv[NR];
@@ -320,12 +329,22 @@ __device__ inline uint32_t topk_threshold_regs(const uint32_t* keys, int NB, int
     kv[s2] = j < NB ? keys[j] : 0u;   // below every real key
   }
   uint32_t thr = 0u;
-  for (int bit = 31; bit >= 0; --bit) {
+  int bit = 31;
+  for (; bit >= 0; --bit) {
     const uint32_t cand = thr | (1u << bit);
     int cnt = 0;
 #pragma unroll
     for (int s2 = 0; s2 < NR; ++s2) cnt += __popcll(__ballot(kv[s2] >= cand));
-    if (cnt >= kk) thr = cand;
+    if (cnt >= kk) {
+      thr = cand;
+      if (cnt == kk) break;
+    }
+  }
+  if (bit >= 0) {   // exactly kk keys are >= thr: the cut is the smallest of them
+    uint32_t m = 0xffffffffu;
+#pragma unroll
+    for (int s2 = 0; s2 < NR; ++s2) m = min(m, kv[s2] >= thr ? kv[s2] : 0xffffffffu);
+    thr = wave_min_u(m);
   }
   gt = 0;
 #pragma unroll
@@ -350,14 +369,23 @@ __device__ inline void topk_cut(const uint32_t* keys, int NB, int lane, int kk, 
   } else if (NB <= 64 * 20) {
     thr = topk_threshold_regs<20>(keys, NB, lane, kk, gt);
   } else {
-    for (int bit = 31; bit >= 0; --bit) {
+    int bit = 31;
+    for (; bit >= 0; --bit) {
       const uint32_t cand = thr | (1u << bit);
       int cnt = 0;
       for (int j0 = 0; j0 < NB; j0 += 64) {
         const int j = j0 + lane;
         cnt += __popcll(__ballot(j < NB && keys[j] >= cand));
       }
-      if (cnt >= kk) thr = cand;
+      if (cnt >= kk) {
+        thr = cand;
+        if (cnt == kk) break;
+      }
+    }
+    if (bit >= 0) {
+      uint32_t m = 0xffffffffu;
+      for (int j = lane; j < NB; j += 64) m = min(m, keys[j] >= thr ? keys[j] : 0xffffffffu);
+      thr = wave_min_u(m);
     }
     for (int j0 = 0; j0 < NB; j0 += 64) {
       const int j = j0 + lane;
