@@ -39,7 +39,12 @@
  *   the same buffers (or both are vsa_plan_noalloc calls on one GPU).
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = null stream).
  *   Work is only enqueued; results are valid once the caller has
- *   synchronized with the stream.
+ *   synchronized with the stream.  Calls enqueue kernel launches and
+ *   nothing else (no memset, copy, allocation or synchronization), so they
+ *   can be captured in a HIP graph on a capturing stream; a captured plan
+ *   that should allocate nothing uses vsa_plan_noalloc, after one eager call
+ *   on the device (its first call on a device looks up the static
+ *   workspace's address).
  * Errors.  Arguments are validated on the host before anything is enqueued;
  *   on error nothing is enqueued and the status says why.  A failed kernel
  *   launch returns VSA_ERR_HIP.  No C++ exception crosses this boundary.
