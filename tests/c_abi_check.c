@@ -44,8 +44,23 @@ int main(void) {
   st = vsa_scheme_workspace(&s, cands, 2, &sws);
   printf("scheme_workspace %d %zu\n", (int)st, sws);
 
-  /* error paths: nothing is enqueued, a status comes back */
+  size_t mws = 0, moff[4] = {0, 0, 0, 0};
+  st = vsa_scheme_means_workspace(&s, cands, 2, &mws, moff);
+  printf("scheme_means_workspace %d %zu %zu %zu %zu %zu\n", (int)st, mws, moff[0], moff[1], moff[2], moff[3]);
+  printf("noalloc_max_ws %zu\n", (size_t)VSA_PLAN_NOALLOC_MAX_WS);
+  printf("calib_limits %zu %d %d\n", (size_t)VSA_CALIB_POOL_BYTES, VSA_CALIB_MAX_WORKGROUPS, VSA_CALIB_MAX_ITERS);
+
+  /* error paths: each fails a host check before anything is enqueued */
   printf("bad_density %d\n", (int)vsa_query(&s, &density, 2, -1, NULL, NULL, NULL, NULL));
+  vsa_index idx = {s, 0, 0, NULL, NULL, 0, 0};
+  int32_t heads[2] = {0, 0};
+  printf("plan_heads_no_list %d\n", (int)vsa_plan_heads(NULL, NULL, NULL, NULL, &s, NULL, 1, &density, 1, -1,
+                                                        &idx, NULL, 0, NULL));
+  printf("plan_heads_repeated %d\n", (int)vsa_plan_heads(NULL, NULL, NULL, NULL, &s, heads, 2, &density, 1, -1,
+                                                         &idx, NULL, 0, NULL));
+  printf("attn_heads_null %d\n", (int)vsa_attn_heads(NULL, NULL, NULL, &idx, heads, 12, 0.0f, NULL, NULL, 0, NULL));
+  printf("plan_noalloc_null %d\n", (int)vsa_plan_noalloc(NULL, NULL, &s, &density, 1, -1, &idx, NULL));
+  printf("calib_null %d\n", (int)vsa_calib_mfma_bf16(NULL, VSA_CALIB_POOL_BYTES, NULL, 1, 1, NULL));
   printf("status_str %s\n", vsa_status_str(VSA_ERR_CAPACITY));
   return 0;
 }

@@ -58,4 +58,15 @@ def test_sizing_matches_binding(c_output):
     assert st == "0" and (int(rl), int(cap), int(pws)) == vsa.query_mixed(shape, opts)
     assert c_output["scheme_workspace"][0] == "0" and int(c_output["scheme_workspace"][1]) > 0
     assert c_output["bad_density"] == [str(_lib.VSA_ERR_INVALID_ARG)]
+    lib = _lib.load()
+    cands = (ctypes.c_int32 * 6)(4, 4, 8, 1, 8, 16)
+    ws, offs = ctypes.c_size_t(), (ctypes.c_size_t * 4)()
+    assert lib.vsa_scheme_means_workspace(ctypes.byref(shape), cands, 2, ctypes.byref(ws), offs) == 0
+    assert c_output["scheme_means_workspace"] == ["0", str(ws.value)] + [str(o) for o in offs]
+    assert int(c_output["noalloc_max_ws"][0]) == _lib.VSA_PLAN_NOALLOC_MAX_WS
+    assert [int(x) for x in c_output["calib_limits"]] == [_lib.VSA_CALIB_POOL_BYTES, _lib.VSA_CALIB_MAX_WORKGROUPS,
+                                                           _lib.VSA_CALIB_MAX_ITERS]
+    bad = str(_lib.VSA_ERR_INVALID_ARG)
+    for key in ("plan_heads_no_list", "plan_heads_repeated", "attn_heads_null", "plan_noalloc_null", "calib_null"):
+        assert c_output[key] == [bad], key
     assert " ".join(c_output["status_str"]) == "index capacity too small"
