@@ -76,9 +76,10 @@ def test_plan_and_attention_over_a_head_subset(vsa, B, heads, window_t):
 CANDS = [(4, 4, 8), (1, 8, 16), (2, 8, 8)]
 
 
-def test_scheme_means_are_the_planner_means(vsa):
-    w = W.custom("scheme_means", 1, 4, 128, (9, 14, 20), (4, 4, 8), "bf16", 0.3, -1, "smooth")
-    _say("[gpu] scheme means against vsa_centroids and vsa_select_scheme")
+@pytest.mark.parametrize("B", [1, 2])
+def test_scheme_means_are_the_planner_means(vsa, B):
+    w = W.custom("scheme_means", B, 4, 128, (9, 14, 20), (4, 4, 8), "bf16", 0.3, -1, "smooth")
+    _say(f"[gpu] scheme means against vsa_centroids and vsa_select_scheme, B={B}")
     inp = W.generate(w, seed=92)
     q, k = _dev(inp["q"]), _dev(inp["k"])
     scores, choice, sm = vsa.select_scheme_means(q, k, w.grid, CANDS)
