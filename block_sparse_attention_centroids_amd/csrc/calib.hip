@@ -6,8 +6,9 @@
 // card can hold that clock depends on power, and power depends on the data
 // the matrix cores switch.  This kernel issues nothing but MFMAs on operands
 // that stay in registers (no memory traffic after the first loads, no LDS,
-// no vector ALU work in the loop), so its rate on random data is the
-// practical ceiling for any bf16 MFMA kernel on the same card.
+// no vector ALU work in the loop), so its rate on data of a given spread is
+// a practical ceiling for bf16 MFMA work on such data on the same card:
+// anything else a kernel does draws on the same power budget.
 //
 // Layout of a wave's work: 8 A and 8 B fragments of v_mfma_f32_32x32x16_bf16
 // (8 bf16 per lane each) loaded once from a 4 MiB pool, then `iters` rounds
